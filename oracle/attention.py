@@ -1,0 +1,97 @@
+"""Sparse MLA decode attention and the split-KV combine, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed ([FlashMLA-18] PR description: d_qk = 576, d_v = 512, top-k
+token records gathered by index with invalid indices and an optional per-head
+attention sink; every query head attends to the same latent):
+
+  for each query row (b, s) and head h, over the valid indices t (index >= 0,
+  duplicates counted as often as they appear):
+      z_t  = softmax_scale * <q_h, K_t>            (K_t: 576-dim dequantized key)
+      m    = max_t z_t,   l = sum_t exp(z_t - m),   LSE = m + ln l
+      O    = sum_t exp(z_t - m) V_t / (l + exp(sink_h - m))   (sink term only
+                                                               when a sink is given)
+  V_t is the first 512 dimensions of K_t.  A row with no valid index has
+  O = 0 and LSE = -inf.  LSE is the natural-log sum over tokens and excludes
+  the sink, so partial results over disjoint index sets can be merged first and
+  the sink applied once afterwards.
+
+Split-KV combine (LSE-weighted merge of partial results over disjoint index
+subsets): LSE = ln sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) O_i divided
+by (1 + exp(sink - LSE)) when a sink is given; all LSE_i = -inf gives O = 0,
+LSE = -inf.  The partial O_i are the sink-free normalised outputs of each
+subset.
+"""
+
+import numpy as np
+
+from .codec import dequantize_records
+from .formats import V_DIM
+
+
+def sparse_decode(q, records, idx, softmax_scale, sink=None):
+    """Reference decode.
+
+    q:       float64 [B, S, H, 576]
+    records: uint8 [R, 352]  -- the token records the indices refer to
+    idx:     int [B, S, topk] -- row numbers into `records`, < 0 = invalid
+    softmax_scale: the float32 scale, used at its exact value
+    sink:    float64 [H] or None
+    returns  O float64 [B, S, H, 512], LSE float64 [B, S, H]
+    """
+    q = np.asarray(q, dtype=np.float64)
+    idx = np.asarray(idx).astype(np.int64)
+    b_, s_, h_, d_ = q.shape
+    kv = dequantize_records(records)
+    scale = float(np.float32(softmax_scale))
+    out = np.zeros((b_, s_, h_, V_DIM))
+    lse = np.full((b_, s_, h_), -np.inf)
+    for b in range(b_):
+        for s in range(s_):
+            valid = idx[b, s][idx[b, s] >= 0]
+            if valid.size == 0:
+                continue
+            k = kv[valid]                       # [n, 576]
+            v = k[:, :V_DIM]                    # [n, 512]
+            z = scale * (q[b, s] @ k.T)         # [H, n]
+            m = z.max(axis=1)
+            e = np.exp(z - m[:, None])
+            l = e.sum(axis=1)
+            lse[b, s] = m + np.log(l)
+            denom = l.copy()
+            if sink is not None:
+                denom = denom + np.exp(np.asarray(sink, dtype=np.float64) - m)
+            out[b, s] = (e @ v) / denom[:, None]
+    return out, lse
+
+
+def partial_decode(q, records, idx, softmax_scale):
+    """Sink-free decode over one index subset: the (O_i, LSE_i) of a split."""
+    return sparse_decode(q, records, idx, softmax_scale, sink=None)
+
+
+def combine(o_parts, lse_parts, sink=None):
+    """Merge split results.
+
+    o_parts:   float64 [P, ..., H, 512]  (sink-free, normalised per split)
+    lse_parts: float64 [P, ..., H]
+    sink:      float64 [H] or None
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    mx = lse_parts.max(axis=0)
+    empty = np.isneginf(mx)
+    safe_mx = np.where(empty, 0.0, mx)
+    w = np.exp(lse_parts - safe_mx)                   # exp(-inf) = 0
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, safe_mx + np.log(np.where(empty, 1.0, tot)))
+    norm_w = np.where(empty, 0.0, w / np.where(empty, 1.0, tot))
+    out = (norm_w[..., None] * o_parts).sum(axis=0)
+    if sink is not None:
+        sink = np.asarray(sink, dtype=np.float64)
+        factor = np.where(empty, 1.0, 1.0 / (1.0 + np.exp(sink - np.where(empty, 0.0, lse))))
+        out = out * factor[..., None]
+    out = np.where(empty[..., None], 0.0, out)
+    return out, lse

@@ -1,0 +1,254 @@
+"""Seeded synthetic inputs for the NVFP4 sparse-MLA decode path.
+
+This module only draws inputs: latents, queries, top-k slot ids, sinks, page
+tables and slot mappings.  It holds none of the method's arithmetic (no
+quantization, no attention), so the test suite can feed the same inputs to the
+HIP library and to the CPU oracle.
+
+Every draw comes from numpy's PCG64 seeded as default_rng([config, stream,
+rep]) with one stream per kind of input:
+  0 channel scales, 1 NoPE latents, 2 RoPE latents, 3 queries,
+  4 indices + invalid mask, 5 sinks, 6 page tables / lengths,
+  7 sentinel cache bytes, 8 slot mapping.
+
+Value distributions (the same for every workload):
+  NoPE  = N(0,1) * channel_scale[d], channel_scale ~ exp(U(ln 0.1, ln 4)) fixed
+          per workload, and each element independently multiplied by 20 with
+          probability 1 %;
+  RoPE  = N(0,1);  Q = N(0,1);  sink = N(0,1) float32 per head.
+All latents and queries are rounded to bfloat16 (round-to-nearest-even).
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+NOPE_DIM = 512
+ROPE_DIM = 64
+QK_DIM = 576
+V_DIM = 512
+RECORD_BYTES = 352
+
+
+def _rng(config_id, stream, rep=0):
+    return np.random.default_rng([config_id, stream, rep])
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def channel_scales(config_id):
+    r = _rng(config_id, 0)
+    return np.exp(r.uniform(np.log(0.1), np.log(4.0), size=NOPE_DIM))
+
+
+def latents(config_id, n, rep=0):
+    """bf16 NoPE [n,512] and RoPE [n,64] latents drawn for n tokens."""
+    cs = channel_scales(config_id)
+    r1 = _rng(config_id, 1, rep)
+    nope = r1.standard_normal((n, NOPE_DIM)) * cs[None, :]
+    outlier = r1.random((n, NOPE_DIM)) < 0.01
+    nope = np.where(outlier, nope * 20.0, nope)
+    rope = _rng(config_id, 2, rep).standard_normal((n, ROPE_DIM))
+    return _bf16(nope), _bf16(rope)
+
+
+@dataclass
+class DecodeWorkload:
+    """One decode step's inputs.
+
+    indices are slot ids into a paged cache of num_blocks pages of block_size
+    tokens (slot = page * block_size + offset); -1 marks an invalid entry.
+    `slots` lists every distinct valid slot the indices (and the step's new
+    tokens) reference, sorted, and latent/rope hold those tokens' latents in
+    that order.  new_slots are the slots of the B*S_q tokens the step appends
+    (the query tokens themselves), a subset of `slots`.
+    """
+    name: str
+    config_id: int
+    batch: int
+    s_q: int
+    h_q: int
+    topk: int
+    block_size: int
+    num_blocks: int
+    softmax_scale: float
+    q: torch.Tensor                      # bf16 [B, S_q, H, 576]
+    indices: np.ndarray                  # int32 [B, S_q, topk]
+    sink: Optional[np.ndarray]           # float32 [H] or None
+    slots: np.ndarray                    # int64 [n] sorted distinct
+    latent: torch.Tensor                 # bf16 [n, 512]
+    rope: torch.Tensor                   # bf16 [n, 64]
+    new_slots: np.ndarray                # int64 [B * S_q]
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_slots(self):
+        return self.num_blocks * self.block_size
+
+    def slot_rows(self, slots):
+        """Row of each slot in `self.slots` (-1 for negative slots)."""
+        slots = np.asarray(slots, dtype=np.int64)
+        rows = np.searchsorted(self.slots, np.maximum(slots, 0))
+        return np.where(slots < 0, -1, rows)
+
+    def new_token_rows(self):
+        return self.slot_rows(self.new_slots)
+
+
+def _page_table(r, pages_per_seq):
+    """Random global page permutation split into per-sequence tables."""
+    total = int(np.sum(pages_per_seq))
+    perm = r.permutation(total)
+    tables, off = [], 0
+    for n in pages_per_seq:
+        tables.append(perm[off:off + n])
+        off += n
+    return tables, total
+
+
+def _finish(name, cid, batch, s_q, h_q, topk, bs, num_blocks, scale, idx,
+            new_slots, with_sink, description, rep=0, extra=None):
+    q = _bf16(_rng(cid, 3, rep).standard_normal((batch, s_q, h_q, QK_DIM)))
+    sink = (_rng(cid, 5, rep).standard_normal(h_q).astype(np.float32)
+            if with_sink else None)
+    used = np.concatenate([idx[idx >= 0].astype(np.int64), new_slots])
+    slots = np.unique(used)
+    latent, rope = latents(cid, len(slots), rep)
+    return DecodeWorkload(name, cid, batch, s_q, h_q, topk, bs, num_blocks,
+                          float(np.float32(scale)), q, idx.astype(np.int32),
+                          sink, slots, latent, rope, new_slots.astype(np.int64),
+                          description, extra or {})
+
+
+def tiny(rep=0):
+    """Batch 1, s_q 1, 16 heads; a 256-token pool (4 pages of 64) that is
+    filled entirely, 64 distinct random indices, no invalid entries, no sink,
+    scale 1/sqrt(576).  The step's new token is the one at position 255."""
+    cid, bs = 0, 64
+    tables, total = _page_table(_rng(cid, 6, rep), [4])
+    pos = _rng(cid, 4, rep).choice(256, size=64, replace=False)
+    idx = (tables[0][pos // bs] * bs + pos % bs).reshape(1, 1, 64)
+    new_slot = np.array([tables[0][255 // bs] * bs + 255 % bs])
+    wl = _finish("tiny", cid, 1, 1, 16, 64, bs, total, 1.0 / 24.0, idx,
+                 new_slot, False,
+                 "tiny codec+decode: B1 S_q1 H16, pool 256, topk 64, no sink",
+                 rep)
+    wl.slots = np.sort((tables[0][:, None] * bs + np.arange(bs)[None, :]).reshape(-1))
+    wl.latent, wl.rope = latents(cid, len(wl.slots), rep)
+    return wl
+
+
+def decode_h64(rep=0, batch=32):
+    """B 32, s_q 1, 64 heads, 32768 tokens per sequence in 64-token pages,
+    random page table, 2048 distinct positions per query, 5 % invalid, sink."""
+    cid, bs, seq, topk = 1, 64, 32768, 2048
+    tables, total = _page_table(_rng(cid, 6, rep), [seq // bs] * batch)
+    r4 = _rng(cid, 4, rep)
+    idx = np.empty((batch, 1, topk), dtype=np.int64)
+    new_slots = np.empty(batch, dtype=np.int64)
+    for b in range(batch):
+        pos = r4.choice(seq, size=topk, replace=False)
+        idx[b, 0] = tables[b][pos // bs] * bs + pos % bs
+        new_slots[b] = tables[b][(seq - 1) // bs] * bs + (seq - 1) % bs
+    inval = r4.random(idx.shape) < 0.05
+    idx[inval] = -1
+    return _finish("decode_h64", cid, batch, 1, 64, topk, bs, total,
+                   1.0 / 24.0, idx, new_slots, True,
+                   f"h_q 64: B{batch} S_q1, 32768-token contexts, topk 2048, "
+                   "5% invalid, sink", rep)
+
+
+def decode_h128_varlen(rep=0, batch=64):
+    """B 64, s_q 1, 128 heads, context length ~ U[4096, 131072], 64-token
+    pages, topk = min(2048, len) distinct positions, 2 % invalid, sink."""
+    cid, bs, topk = 2, 64, 2048
+    r6 = _rng(cid, 6, rep)
+    lens = r6.integers(4096, 131072, endpoint=True, size=batch)
+    pages = [int(-(-int(n) // bs)) for n in lens]
+    tables, total = _page_table(r6, pages)
+    r4 = _rng(cid, 4, rep)
+    idx = np.empty((batch, 1, topk), dtype=np.int64)
+    new_slots = np.empty(batch, dtype=np.int64)
+    for b in range(batch):
+        n = int(lens[b])
+        k = min(topk, n)
+        pos = r4.choice(n, size=k, replace=False)
+        row = np.full(topk, -1, dtype=np.int64)
+        row[:k] = tables[b][pos // bs] * bs + pos % bs
+        idx[b, 0] = row
+        new_slots[b] = tables[b][(n - 1) // bs] * bs + (n - 1) % bs
+    inval = r4.random(idx.shape) < 0.02
+    idx[inval] = -1
+    return _finish("decode_h128_varlen", cid, batch, 1, 128, topk, bs, total,
+                   1.0 / 24.0, idx, new_slots, True,
+                   f"h_q 128 varlen: B{batch} S_q1, lengths U[4096,131072], "
+                   "topk 2048, 2% invalid, sink", rep,
+                   extra={"lengths": lens})
+
+
+def decode_h16_mtp(rep=0, batch=256):
+    """B 256, s_q 2 (MTP), 16 heads, 65536-token contexts, 64-token pages.
+    Query j sits at position L-2+j; its 640 indices are the 128-token window
+    ending at that position followed by 512 distinct positions drawn from the
+    older history; 3 % invalid; sink."""
+    cid, bs, seq, s_q, win, extra_k = 4, 64, 65536, 2, 128, 512
+    topk = win + extra_k
+    tables, total = _page_table(_rng(cid, 6, rep), [seq // bs] * batch)
+    r4 = _rng(cid, 4, rep)
+    idx = np.empty((batch, s_q, topk), dtype=np.int64)
+    new_slots = np.empty(batch * s_q, dtype=np.int64)
+    for b in range(batch):
+        for j in range(s_q):
+            p = seq - s_q + j
+            window = np.arange(p - win + 1, p + 1)
+            hist = r4.choice(p - win + 1, size=extra_k, replace=False)
+            pos = np.concatenate([window, hist])
+            idx[b, j] = tables[b][pos // bs] * bs + pos % bs
+            new_slots[b * s_q + j] = tables[b][p // bs] * bs + p % bs
+    inval = r4.random(idx.shape) < 0.03
+    idx[inval] = -1
+    return _finish("decode_h16_mtp", cid, batch, s_q, 16, topk, bs, total,
+                   1.0 / 24.0, idx, new_slots, True,
+                   f"h_q 16 MTP: B{batch} S_q2, 65536-token contexts, topk 640 "
+                   "(128 window + 512 history), 3% invalid, sink", rep)
+
+
+@dataclass
+class AppendWorkload:
+    """Quantize-append inputs: N new tokens scattered into a sentinel-filled
+    cache of num_blocks pages by a slot mapping with -1 entries."""
+    name: str
+    num_tokens: int
+    block_size: int
+    num_blocks: int
+    latent: torch.Tensor          # bf16 [N, 512]
+    rope: torch.Tensor            # bf16 [N, 64]
+    slot_mapping: np.ndarray      # int64 [N]
+    sentinel: np.ndarray          # uint8 [num_blocks * block_size, 352]
+
+
+def append_write(rep=0, num_tokens=16384, num_slots=262144, p_skip=0.10):
+    """16384 tokens into a 262144-slot cache, 10 % of slots -1, the rest
+    distinct uniform slots; the cache starts as random sentinel bytes."""
+    cid, bs = 3, 64
+    latent, rope = latents(cid, num_tokens, rep)
+    r8 = _rng(cid, 8, rep)
+    sm = r8.choice(num_slots, size=num_tokens, replace=False).astype(np.int64)
+    sm[r8.random(num_tokens) < p_skip] = -1
+    sentinel = _rng(cid, 7, rep).integers(0, 256, size=(num_slots, RECORD_BYTES),
+                                          dtype=np.uint8)
+    return AppendWorkload("append_write", num_tokens, bs, num_slots // bs,
+                          latent, rope, sm, sentinel)
+
+
+DECODE_WORKLOADS = {
+    "tiny": tiny,
+    "decode_h64": decode_h64,
+    "decode_h128_varlen": decode_h128_varlen,
+    "decode_h16_mtp": decode_h16_mtp,
+}
