@@ -1,0 +1,219 @@
+"""MI355X (gfx950) NVFP4 sparse-MLA decode: thin Python binding.
+
+Every step of the path runs in the HIP kernels of libnvfp4_mla.so behind the C
+ABI declared in include/nvfp4_mla.h; this module only marshals torch tensors
+(device memory and the current stream) into those calls and turns error codes
+into exceptions.  There is no fallback: if the library is not built, or the
+device is not gfx950, every call raises.
+
+Build the library with ``python -m sparse_mla_decode_nvfp4_amd.build``.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4_mla.so")
+
+RECORD_BYTES = 352
+NOPE_DIM = 512
+ROPE_DIM = 64
+QK_DIM = 576
+V_DIM = 512
+MAX_SPLITS = 64
+
+OK = 0
+ERR_INVALID_ARGUMENT = -1
+ERR_UNSUPPORTED_FORMAT = -2
+ERR_UNSUPPORTED_DEVICE = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+ERR_HIP = -5
+
+# exported symbol -> (restype, argtypes)
+_P, _I32, _I64, _SZ, _F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_size_t, ctypes.c_float)
+SIGNATURES = {
+    "nvfp4_mla_abi_version": (ctypes.c_int, []),
+    "nvfp4_mla_last_error": (ctypes.c_char_p, []),
+    "nvfp4_mla_check_format": (ctypes.c_int, [_I32, _I32, _I32, _I32]),
+    "nvfp4_mla_quantize_append": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I32,
+                                                 _I64, _P]),
+    "nvfp4_mla_dequantize_gather": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _I64, _P, _P]),
+    "nvfp4_mla_sparse_decode_plan": (ctypes.c_int, [_I32, _I32, _I32, _I32,
+                                                    ctypes.POINTER(ctypes.c_int32)]),
+    "nvfp4_mla_sparse_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "nvfp4_mla_sparse_decode": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32, _I32, _I32,
+                                               _I32, _P, _F32, _P, _P, _P, _SZ, _I32, _P]),
+    "nvfp4_mla_combine": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _P, _P, _P, _P]),
+}
+
+_lib_handle = None
+
+
+class NativeLibraryMissing(ImportError):
+    pass
+
+
+class Nvfp4MlaError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """The loaded C library (loads it on first use; raises if not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise NativeLibraryMissing(
+                f"{LIB_PATH} is not built; run python -m sparse_mla_decode_nvfp4_amd.build")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def last_error():
+    return lib().nvfp4_mla_last_error().decode()
+
+
+def _check(fn, code):
+    if code != OK:
+        raise Nvfp4MlaError(fn, code, last_error())
+
+
+def abi_version():
+    return lib().nvfp4_mla_abi_version()
+
+
+def check_format(record_bytes=RECORD_BYTES, nope_dim=NOPE_DIM, rope_dim=ROPE_DIM, v_dim=V_DIM):
+    _check("nvfp4_mla_check_format",
+           lib().nvfp4_mla_check_format(record_bytes, nope_dim, rope_dim, v_dim))
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _cache_geometry(kv_cache):
+    """(num_blocks, block_size, block_stride_bytes) of a [blocks, block_size,
+    352] uint8 cache tensor (pages may be padded: stride(0) >= block_size*352)."""
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 3 or kv_cache.shape[2] != RECORD_BYTES:
+        raise ValueError("kv_cache must be a uint8 tensor [num_blocks, block_size, 352]")
+    if kv_cache.stride(2) != 1 or kv_cache.stride(1) != RECORD_BYTES:
+        raise ValueError("records within a page must be contiguous 352-byte rows")
+    return kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0)
+
+
+def new_cache(num_blocks, block_size, device="cuda", fill=0):
+    """A zero-filled (or `fill`-filled) paged cache [num_blocks, block_size, 352]."""
+    return torch.full((num_blocks, block_size, RECORD_BYTES), fill, dtype=torch.uint8,
+                      device=device)
+
+
+def quantize_append(latent, rope, slot_mapping, kv_cache):
+    """Writes NVFP4 records for each token with slot_mapping >= 0, in place.
+
+    latent: bf16 [N, >=512] (rows 16-byte aligned), rope: bf16 [N, >=64],
+    slot_mapping: int64 [N], kv_cache: uint8 [num_blocks, block_size, 352].
+    """
+    n = latent.shape[0]
+    if latent.dtype != torch.bfloat16 or rope.dtype != torch.bfloat16:
+        raise ValueError("latent and rope must be bfloat16")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n or rope.shape[0] != n:
+        raise ValueError("slot_mapping must be int64 [N] matching latent/rope rows")
+    if latent.stride(-1) != 1 or rope.stride(-1) != 1 or not slot_mapping.is_contiguous():
+        raise ValueError("inner dimensions must be contiguous")
+    nb, bs, stride = _cache_geometry(kv_cache)
+    code = lib().nvfp4_mla_quantize_append(
+        _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(slot_mapping), n,
+        _ptr(kv_cache), nb, bs, stride, _stream(kv_cache.device))
+    _check("nvfp4_mla_quantize_append", code)
+    return kv_cache
+
+
+def dequantize_gather(kv_cache, slots, out=None):
+    """bf16 [n, 576] dequantized keys of the records at `slots` (int32)."""
+    if slots.dtype != torch.int32 or not slots.is_contiguous():
+        raise ValueError("slots must be a contiguous int32 tensor")
+    n = slots.numel()
+    if out is None:
+        out = torch.empty((n, QK_DIM), dtype=torch.bfloat16, device=kv_cache.device)
+    nb, bs, stride = _cache_geometry(kv_cache)
+    code = lib().nvfp4_mla_dequantize_gather(_ptr(kv_cache), nb, bs, stride, _ptr(slots), n,
+                                             _ptr(out), _stream(kv_cache.device))
+    _check("nvfp4_mla_dequantize_gather", code)
+    return out
+
+
+def plan(batch, s_q, h_q, topk):
+    out = ctypes.c_int32(0)
+    _check("nvfp4_mla_sparse_decode_plan",
+           lib().nvfp4_mla_sparse_decode_plan(batch, s_q, h_q, topk, ctypes.byref(out)))
+    return out.value
+
+
+def workspace_size(batch, s_q, h_q, topk, num_splits=0):
+    n = lib().nvfp4_mla_sparse_decode_workspace_size(batch, s_q, h_q, topk, num_splits)
+    err = last_error()
+    if err:
+        raise Nvfp4MlaError("nvfp4_mla_sparse_decode_workspace_size", ERR_INVALID_ARGUMENT, err)
+    return n
+
+
+def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
+                  workspace=None, out=None, lse=None):
+    """Sparse MLA decode.  q: bf16 [B, S_q, H, 576]; indices: int32 [B, S_q, topk]
+    slot ids (< 0 invalid); sink: float32 [H] or None.  Returns (O bf16
+    [B, S_q, H, 512], LSE float32 [B, S_q, H])."""
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[-1] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, S_q, H, 576] tensor")
+    b, s, h, _ = q.shape
+    if (indices.dtype != torch.int32 or indices.dim() != 3 or tuple(indices.shape[:2]) != (b, s)
+            or not indices.is_contiguous()):
+        raise ValueError("indices must be a contiguous int32 [B, S_q, topk] tensor")
+    topk = indices.shape[2]
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
+        raise ValueError("sink must be float32 [H]")
+    if num_splits == 0:
+        num_splits = plan(b, s, h, topk)
+    need = workspace_size(b, s, h, topk, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, s, h), dtype=torch.float32, device=q.device)
+    nb, bs, stride = _cache_geometry(kv_cache)
+    code = lib().nvfp4_mla_sparse_decode(
+        _ptr(q), _ptr(kv_cache), nb, bs, stride, _ptr(indices), b, s, h, topk, _ptr(sink),
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
+    _check("nvfp4_mla_sparse_decode", code)
+    return out, lse
+
+
+def combine(o_partial, lse_partial, sink=None, out=None, lse=None):
+    """LSE-weighted merge.  o_partial float32 [P, R, H, 512], lse_partial float32
+    [P, R, H].  Returns (O bf16 [R, H, 512], LSE float32 [R, H])."""
+    o_partial = o_partial.contiguous()
+    lse_partial = lse_partial.contiguous()
+    p, r, h, _ = o_partial.shape
+    if out is None:
+        out = torch.empty((r, h, V_DIM), dtype=torch.bfloat16, device=o_partial.device)
+    if lse is None:
+        lse = torch.empty((r, h), dtype=torch.float32, device=o_partial.device)
+    code = lib().nvfp4_mla_combine(_ptr(o_partial), _ptr(lse_partial),
+                                   p, r, h, _ptr(sink), _ptr(out), _ptr(lse),
+                                   _stream(o_partial.device))
+    _check("nvfp4_mla_combine", code)
+    return out, lse

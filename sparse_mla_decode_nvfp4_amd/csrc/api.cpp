@@ -1,0 +1,359 @@
+// C ABI of the NVFP4 sparse-MLA library (declared in include/nvfp4_mla.h):
+// argument validation, the gfx950 device gate, the split planner, workspace
+// sizing, the thread-local error message, and the kernel launches.
+//
+// Every argument is validated before the first HIP call, so argument errors
+// are reported identically with or without a GPU.  Failures are loud: each has
+// its own status code and message (the convention of the pages' write path,
+// which rejects unsupported dims and devices with explicit errors).
+#include "../../include/nvfp4_mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return NVFP4_MLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device cache: 0 = not yet checked, 1 = gfx950, 2 = other.  Zero-
+// initialised statics; racing first calls both store the same values.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Returns OK when the current device is gfx950; fills cus when non-null.
+int check_device(int* cus) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_DEVICE, "no HIP device available (%s)",
+                hipGetErrorString(e));
+  if (dev >= kMaxDevices)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
+  int known = g_dev_state[dev].load(std::memory_order_acquire);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(NVFP4_MLA_ERR_UNSUPPORTED_DEVICE, "hipGetDeviceProperties failed: %s",
+                  hipGetErrorString(e));
+    const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    known = is950 ? 1 : 2;
+    g_dev_state[dev].store(known, std::memory_order_release);
+    if (!is950)
+      return fail(NVFP4_MLA_ERR_UNSUPPORTED_DEVICE,
+                  "device %d is %s; this library is built for gfx950 (MI355X) only", dev,
+                  prop.gcnArchName);
+  }
+  if (known != 1)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_DEVICE,
+                "device %d is not gfx950; this library is built for gfx950 (MI355X) only", dev);
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return NVFP4_MLA_OK;
+}
+
+int check_cache(const void* kv_cache, int64_t num_blocks, int32_t block_size,
+                int64_t block_stride_bytes, int64_t* num_slots) {
+  if (kv_cache == nullptr) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "kv_cache is NULL");
+  if (!aligned(kv_cache, 16))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "kv_cache must be 16-byte aligned");
+  if (num_blocks < 1) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_blocks must be >= 1");
+  if (block_size < 1) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "block_size must be >= 1");
+  if (block_stride_bytes % 16 != 0)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "block_stride_bytes must be a multiple of 16");
+  if (block_stride_bytes < (int64_t)block_size * NVFP4_MLA_RECORD_BYTES)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                "block_stride_bytes %lld < block_size * 352 = %lld",
+                (long long)block_stride_bytes, (long long)block_size * NVFP4_MLA_RECORD_BYTES);
+  const int64_t slots = num_blocks * (int64_t)block_size;
+  if (num_blocks > INT64_C(0x7FFFFFFF) || slots > INT64_C(0x7FFFFFFF))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                "num_blocks * block_size = %lld exceeds the 2^31-1 slot ids int32 indices address",
+                (long long)slots);
+  *num_slots = slots;
+  return NVFP4_MLA_OK;
+}
+
+nvfp4::PageAddr make_page_addr(int32_t block_size, int64_t block_stride_bytes) {
+  nvfp4::PageAddr pa{};
+  pa.block_stride = (uint64_t)block_stride_bytes;
+  pa.block_size = (uint32_t)block_size;
+  pa.pow2 = (block_size & (block_size - 1)) == 0;
+  pa.shift = 0;
+  while ((1u << pa.shift) < (uint32_t)block_size) pa.shift++;
+  // ceil(2^64 / d) for d >= 2 that is not a power of two
+  if (!pa.pow2) {
+    const unsigned __int128 one = (unsigned __int128)1 << 64;
+    pa.recip = (uint64_t)((one + block_size - 1) / (unsigned __int128)block_size);
+  }
+  return pa;
+}
+
+int check_decode_shape(int32_t batch, int32_t s_q, int32_t h_q, int32_t topk) {
+  if (batch < 0 || s_q < 0)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "batch and s_q must be >= 0");
+  if ((int64_t)batch * s_q > INT64_C(0x7FFFFFFF))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "batch * s_q too large");
+  if (h_q < 16 || h_q > 256 || h_q % 16 != 0)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "h_q = %d must be a multiple of 16 in [16, 256]",
+                h_q);
+  if (topk < 1 || topk > 65536)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d must be in [1, 65536]", topk);
+  return NVFP4_MLA_OK;
+}
+
+// Deterministic split choice: enough workgroups for two per CU, each split
+// keeping at least four 16-token blocks per wave-set.
+int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
+  const int64_t wgs = (int64_t)rows * (h_q / 16);
+  const int nblk = (topk + 15) / 16;
+  if (wgs == 0) return 1;
+  int64_t want = (2 * (int64_t)cus + wgs - 1) / wgs;
+  const int64_t max_by_work = nblk / 4 > 0 ? nblk / 4 : 1;
+  if (want > max_by_work) want = max_by_work;
+  if (want > NVFP4_MLA_MAX_SPLITS) want = NVFP4_MLA_MAX_SPLITS;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+size_t workspace_bytes(int64_t rows, int32_t h_q, int32_t splits) {
+  if (splits <= 1) return 0;
+  const size_t o = (size_t)splits * rows * h_q * NVFP4_MLA_V_DIM * sizeof(float);
+  const size_t o_al = (o + 255) & ~(size_t)255;
+  return o_al + (size_t)splits * rows * h_q * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_mla_abi_version(void) { return NVFP4_MLA_ABI_VERSION; }
+
+const char* nvfp4_mla_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_mla_check_format(int32_t record_bytes, int32_t nope_dim, int32_t rope_dim,
+                           int32_t v_dim) {
+  if (record_bytes != NVFP4_MLA_RECORD_BYTES || nope_dim != NVFP4_MLA_NOPE_DIM ||
+      rope_dim != NVFP4_MLA_ROPE_DIM || v_dim != NVFP4_MLA_V_DIM)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_FORMAT,
+                "unsupported format: record %d B, NoPE %d, RoPE %d, d_v %d (this library "
+                "implements the 352 B NVFP4 record with 512/64/512)",
+                record_bytes, nope_dim, rope_dim, v_dim);
+  return ok();
+}
+
+int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride,
+                              const void* rope_bf16, int64_t rope_row_stride,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                              int64_t block_stride_bytes, void* stream) {
+  if (num_tokens < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  int64_t num_slots = 0;
+  int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  if (rc) return rc;
+  if (num_tokens > 0) {
+    if (!latent_bf16 || !rope_bf16 || !slot_mapping)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "latent, rope and slot_mapping must be non-NULL");
+    if (latent_row_stride < NVFP4_MLA_NOPE_DIM || rope_row_stride < NVFP4_MLA_ROPE_DIM)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "row strides (%lld, %lld) must be >= (512, 64) elements",
+                  (long long)latent_row_stride, (long long)rope_row_stride);
+    if (!aligned(latent_bf16, 16) || latent_row_stride % 8 != 0)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "latent rows must be 16-byte aligned (aligned base, stride multiple of 8)");
+    if (!aligned(rope_bf16, 2) || !aligned(slot_mapping, 8))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "rope / slot_mapping misaligned");
+    if (num_tokens > (int64_t)0x7FFFFFFF * 4)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens too large");
+  }
+  rc = check_device(nullptr);
+  if (rc) return rc;
+  hipError_t e = nvfp4::launch_quantize_append(
+      static_cast<const uint16_t*>(latent_bf16), latent_row_stride,
+      static_cast<const uint16_t*>(rope_bf16), rope_row_stride, slot_mapping, num_tokens, kv_cache,
+      num_slots, make_page_addr(block_size, block_stride_bytes),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(NVFP4_MLA_ERR_HIP, "quantize_append launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                                int64_t block_stride_bytes, const int32_t* slots, int64_t n,
+                                void* out_bf16, void* stream) {
+  if (n < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  int64_t num_slots = 0;
+  int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  if (rc) return rc;
+  if (n > 0) {
+    if (!slots || !out_bf16)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "slots and out must be non-NULL");
+    if (!aligned(out_bf16, 16) || !aligned(slots, 4))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+    if (n > (int64_t)0x7FFFFFFF * 4)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "n too large");
+  }
+  rc = check_device(nullptr);
+  if (rc) return rc;
+  hipError_t e = nvfp4::launch_dequantize_gather(kv_cache, num_slots,
+                                                 make_page_addr(block_size, block_stride_bytes),
+                                                 slots, n, static_cast<uint16_t*>(out_bf16),
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(NVFP4_MLA_ERR_HIP, "dequantize_gather launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
+                                 int32_t* num_splits_out) {
+  if (!num_splits_out) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits_out is NULL");
+  int rc = check_decode_shape(batch, s_q, h_q, topk);
+  if (rc) return rc;
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+  *num_splits_out = plan_splits(batch * s_q, h_q, topk, cus);
+  return ok();
+}
+
+size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q, int32_t h_q,
+                                              int32_t topk, int32_t num_splits) {
+  if (check_decode_shape(batch, s_q, h_q, topk)) return 0;
+  if (num_splits < 0 || num_splits > NVFP4_MLA_MAX_SPLITS) {
+    fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d out of [0, %d]", num_splits,
+         NVFP4_MLA_MAX_SPLITS);
+    return 0;
+  }
+  int splits = num_splits;
+  if (splits == 0) {
+    int cus = 0;
+    if (check_device(&cus)) return 0;
+    splits = plan_splits(batch * s_q, h_q, topk, cus);
+  }
+  ok();
+  return workspace_bytes((int64_t)batch * s_q, h_q, splits);
+}
+
+int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache, int64_t num_blocks,
+                            int32_t block_size, int64_t block_stride_bytes,
+                            const int32_t* indices, int32_t batch, int32_t s_q, int32_t h_q,
+                            int32_t topk, const float* attn_sink, float softmax_scale,
+                            void* out_bf16, float* lse, void* workspace, size_t workspace_bytes_in,
+                            int32_t num_splits, void* stream) {
+  int rc = check_decode_shape(batch, s_q, h_q, topk);
+  if (rc) return rc;
+  int64_t num_slots = 0;
+  rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  if (rc) return rc;
+  if (num_splits < 0 || num_splits > NVFP4_MLA_MAX_SPLITS)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d out of [0, %d]", num_splits,
+                NVFP4_MLA_MAX_SPLITS);
+  if (!std::isfinite(softmax_scale))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  const int64_t rows = (int64_t)batch * s_q;
+  if (rows > 0) {
+    if (!q_bf16 || !indices || !out_bf16 || !lse)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "q, indices, out and lse must be non-NULL");
+    if (!aligned(q_bf16, 16) || !aligned(out_bf16, 16) || !aligned(lse, 4) ||
+        !aligned(indices, 4) || (attn_sink && !aligned(attn_sink, 4)))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "q and out must be 16-byte aligned; indices, lse, sink 4-byte aligned");
+  }
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+  int splits = num_splits == 0 ? plan_splits((int32_t)rows, h_q, topk, cus) : num_splits;
+  const size_t need = workspace_bytes(rows, h_q, splits);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes_in < need)
+      return fail(NVFP4_MLA_ERR_WORKSPACE_TOO_SMALL,
+                  "decode with %d splits needs %zu workspace bytes, got %zu", splits, need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes_in);
+    if (!aligned(workspace, 256))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+  if (rows == 0) return ok();
+  nvfp4::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.cache = kv_cache;
+  a.pa = make_page_addr(block_size, block_stride_bytes);
+  a.num_slots = num_slots;
+  a.indices = indices;
+  a.rows = (int32_t)rows;
+  a.h_q = h_q;
+  a.topk = topk;
+  a.sink = attn_sink;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.lse = lse;
+  a.splits = splits;
+  if (splits > 1) {
+    const size_t o = (size_t)splits * rows * h_q * NVFP4_MLA_V_DIM * sizeof(float);
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o + 255) & ~(size_t)255));
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = nvfp4::launch_decode(a, st);
+  if (e != hipSuccess)
+    return fail(NVFP4_MLA_ERR_HIP, "sparse_decode launch failed: %s", hipGetErrorString(e));
+  if (splits > 1) {
+    e = nvfp4::launch_combine(a.o_part, a.lse_part, splits, rows, h_q, attn_sink, a.out, lse, st);
+    if (e != hipSuccess)
+      return fail(NVFP4_MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int nvfp4_mla_combine(const float* o_partial, const float* lse_partial, int32_t num_splits,
+                      int64_t rows, int32_t h_q, const float* attn_sink, void* out_bf16,
+                      float* lse, void* stream) {
+  if (num_splits < 1 || num_splits > 4096)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d must be in [1, 4096]", num_splits);
+  if (rows < 0 || h_q < 1)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "rows must be >= 0 and h_q >= 1");
+  if (rows * (int64_t)h_q > INT64_C(0x7FFFFFFF))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "rows * h_q too large");
+  if (rows > 0) {
+    if (!o_partial || !lse_partial || !out_bf16 || !lse)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "o_partial, lse_partial, out, lse must be non-NULL");
+    if (!aligned(o_partial, 16) || !aligned(out_bf16, 8) || !aligned(lse_partial, 4) ||
+        !aligned(lse, 4) || (attn_sink && !aligned(attn_sink, 4)))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  }
+  int rc = check_device(nullptr);
+  if (rc) return rc;
+  hipError_t e = nvfp4::launch_combine(o_partial, lse_partial, num_splits, rows, h_q, attn_sink,
+                                       static_cast<uint16_t*>(out_bf16), lse,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(NVFP4_MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// Quantize-append (write path) and dequantize-gather kernels for the 352-byte
+// NVFP4 record.  gfx950.
+//
+// Write rule (vLLM PR #82 "kv: nvfp4_ds_mla -- 4-bit NVFP4 KV cache for B12X
+// sparse MLA (SM120)", Fix and Tests; layout from FlashMLA PR #18, PR
+// description): per 16-element NoPE block, scale S = E4M3(amax/6) rounded to
+// nearest-even and saturated at 448; each element's magnitude is rounded to
+// the nearest E2M1 grid point of |x|/value(S) (ties to the even code, 0 when
+// the scale is 0), its sign copied; RoPE is stored as unscaled E4M3 (RNE,
+// saturating, sign kept).  Tokens whose slot is negative are skipped.
+#include "device_common.h"
+#include "launch.h"
+
+namespace nvfp4 {
+
+// E4M3 code of a non-negative finite fp32 value, round-to-nearest-even on the
+// finite grid, saturating to 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne_sat_mag(float q) {
+  q = fminf(q, 448.0f);
+  if (q < 0.015625f) {                       // below 2^-6: subnormal grid m * 2^-9
+    return (uint32_t)__builtin_rintf(q * 512.0f);   // 8 -> 0x08 (= 2^-6) is right too
+  }
+  uint32_t b = __float_as_uint(q);
+  b += 0x7FFFFu + ((b >> 20) & 1u);          // RNE of the mantissa to 3 bits
+  return (b >> 20) - (120u << 3);            // rebias exponent 127 -> 7
+}
+
+// Magnitude code (0..7) of |x| on the E2M1 grid {0,.5,1,1.5,2,3,4,6} * s,
+// ties to the even code.  Thresholds s*{.25,.75,1.25,1.75,2.5,3.5,5} are exact
+// fp32 products; a tie rounds toward the even code, hence > vs >=.
+__device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
+  uint32_t c = (a > 0.25f * s) + (a >= 0.75f * s) + (a > 1.25f * s) +
+               (a >= 1.75f * s) + (a > 2.5f * s) + (a >= 3.5f * s) + (a > 5.0f * s);
+  return s == 0.0f ? 0u : c;
+}
+
+// One wavefront per token; 4 tokens per 256-thread block.  Lane l quantizes
+// NoPE elements [8l, 8l+8) (block l/2) and RoPE element l; the record is
+// assembled in LDS and written with 22 16-byte stores.
+__global__ void __launch_bounds__(256)
+quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
+                       const uint16_t* __restrict__ rope, int64_t rstride,
+                       const int64_t* __restrict__ slot_mapping, int64_t num_tokens,
+                       uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa) {
+  __shared__ __attribute__((aligned(16))) uint8_t rec[4][kRecordBytes];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
+  if (tok >= num_tokens) return;
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;          // wave-uniform skip
+
+  uint8_t* r = rec[wave];
+  // ---- NoPE: 8 elements per lane, two lanes per 16-element block
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(latent + tok * lstride + 8 * lane);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = __uint_as_float(raw[i] << 16);
+    x[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const uint32_t scode = e4m3_rne_sat_mag(__fdiv_rn(amax, 6.0f));
+  const float sv = e4m3x2_to_f32<0>(scode).x;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint32_t code = e2m1_mag(fabsf(x[i]), sv) | ((__float_as_uint(x[i]) >> 28) & 8u);
+    packed |= code << (4 * i);
+  }
+  reinterpret_cast<uint32_t*>(r)[lane] = packed;
+  if ((lane & 1) == 0) r[kScaleOffset + scale_byte(lane >> 1)] = (uint8_t)scode;
+  // ---- RoPE: lane l handles element l
+  const float rv = __uint_as_float((uint32_t)rope[tok * rstride + lane] << 16);
+  const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
+  r[kRopeOffset + lane] = (uint8_t)rcode;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  if (lane < kRecordBytes / 16) {
+    uint8_t* dst = cache + pa.offset((uint32_t)slot);
+    reinterpret_cast<u32x4*>(dst)[lane] = reinterpret_cast<const u32x4*>(r)[lane];
+  }
+}
+
+// One wavefront per output row: lane l dequantizes NoPE elements [8l, 8l+8)
+// through the decode's own routine; lanes 0..7 produce the 64 RoPE values.
+__global__ void __launch_bounds__(256)
+dequantize_gather_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa,
+                         const int32_t* __restrict__ slots, int64_t n,
+                         uint16_t* __restrict__ out) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= n) return;
+  const int32_t slot = slots[row];
+  u32x4* dst = reinterpret_cast<u32x4*>(out + row * kQkDim);
+  if (slot < 0 || (int64_t)slot >= num_slots) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    dst[lane] = z;
+    if (lane < 8) dst[64 + lane] = z;
+    return;
+  }
+  const uint8_t* src = cache + pa.offset((uint32_t)slot);
+  const uint32_t nib = reinterpret_cast<const uint32_t*>(src)[lane];
+  const int s = lane >> 1;
+  const float sv = e4m3x2_to_f32<0>((uint32_t)src[kScaleOffset + scale_byte(s)]).x;
+  uint32_t o[4];
+  dequant8(nib, sv, o);
+  const u32x4 ov = {o[0], o[1], o[2], o[3]};
+  dst[lane] = ov;
+  if (lane < 8) {
+    const u32x2 rb = reinterpret_cast<const u32x2*>(src + kRopeOffset)[lane];
+    const u32x4 rv = {e4m3x2_to_bf16x2<0>(rb.x), e4m3x2_to_bf16x2<1>(rb.x),
+                      e4m3x2_to_bf16x2<0>(rb.y), e4m3x2_to_bf16x2<1>(rb.y)};
+    dst[64 + lane] = rv;
+  }
+}
+
+hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
+                                  const uint16_t* rope, int64_t rstride,
+                                  const int64_t* slot_mapping, int64_t num_tokens,
+                                  uint8_t* cache, int64_t num_slots, const PageAddr& pa,
+                                  hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t blocks = (num_tokens + 3) / 4;
+  hipLaunchKernelGGL(quantize_append_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
+                     num_slots, pa);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_gather(const uint8_t* cache, int64_t num_slots, const PageAddr& pa,
+                                    const int32_t* slots, int64_t n, uint16_t* out,
+                                    hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 3) / 4;
+  hipLaunchKernelGGL(dequantize_gather_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     cache, num_slots, pa, slots, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,100 @@
+// Device-side helpers shared by the codec, dequantize-gather and decode
+// kernels: the 352-byte record layout, exact E2M1/E4M3 -> bf16 dequantization
+// and slot -> record addressing.  gfx950 only.
+//
+// Record layout (FlashMLA PR #18 "W4A16 DSA: NVFP4 KV cache format for SM100
+// sparse decode", PR description): bytes [0,256) hold 512 E2M1 NoPE codes two
+// per byte (element 2j in the low nibble of byte j), [256,320) 64 unscaled
+// E4M3 RoPE values, [320,352) 32 E4M3 block scales with the scale of 16-element
+// block s at byte 320 + 8*(s&3) + (s>>2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kRecordBytes = 352;
+constexpr int kNopeDim = 512;
+constexpr int kRopeDim = 64;
+constexpr int kQkDim = 576;
+constexpr int kVDim = 512;
+constexpr int kNopeBytes = 256;
+constexpr int kRopeOffset = 256;
+constexpr int kScaleOffset = 320;
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// Byte of the scale area holding NoPE block s (the 8x4 -> 4x8 transpose).
+__host__ __device__ constexpr int scale_byte(int s) { return 8 * (s & 3) + (s >> 2); }
+
+// Two packed bf16 from the upper halves of two fp32 values.  Exact whenever
+// both values are bf16-representable (true for every dequantized value).
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Two E4M3 bytes (selected 16-bit word of `w`) -> two fp32, exact.  The
+// scaled-convert's scale is 1.0, so its exponent-only scaling is the identity.
+template <int kWord>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, kWord != 0);
+}
+
+// Two E4M3 bytes -> two packed bf16 (one dword), exact.
+template <int kWord>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kWord != 0);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// one block scale -> eight bf16 (four dwords, element order).  Every product
+// e2m1 * e4m3 has at most 6 significant bits and lies in [2^-10, 2688], so the
+// fp32 products are exact and truncation to bf16 is exact.  The fp4 convert
+// runs with scale 1.0 (its scale operand applies only an exponent).
+__device__ __forceinline__ void dequant8(uint32_t nib, float scale, uint32_t out[4]) {
+  f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
+  f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 1);
+  f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 2);
+  f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 3);
+  out[0] = pack_bf16_trunc(a.x * scale, a.y * scale);
+  out[1] = pack_bf16_trunc(b.x * scale, b.y * scale);
+  out[2] = pack_bf16_trunc(c.x * scale, c.y * scale);
+  out[3] = pack_bf16_trunc(d.x * scale, d.y * scale);
+}
+
+// Slot -> byte offset of its record in the paged cache.  Pages of
+// `block_size` records start every `block_stride` bytes.  Power-of-two page
+// sizes use shift/mask; others use a 64-bit reciprocal (exact for every
+// 32-bit slot: floor(n * ceil(2^64/d) / 2^64) == n / d).
+struct PageAddr {
+  uint64_t block_stride;
+  uint64_t recip;        // ceil(2^64 / block_size), unused for powers of two
+  uint32_t block_size;
+  uint32_t shift;        // log2(block_size) when pow2
+  uint32_t pow2;
+  __device__ __forceinline__ uint64_t offset(uint32_t slot) const {
+    uint32_t page, off;
+    if (pow2) {
+      page = slot >> shift;
+      off = slot & (block_size - 1);
+    } else if (block_size == 1) {
+      page = slot;
+      off = 0;
+    } else {
+      page = (uint32_t)__umul64hi((uint64_t)slot, recip);
+      off = slot - page * block_size;
+    }
+    return (uint64_t)page * block_stride + (uint64_t)off * kRecordBytes;
+  }
+};
+
+}  // namespace nvfp4

@@ -1,0 +1,46 @@
+// Internal launchers behind the C ABI (include/nvfp4_mla.h).  Arguments are
+// validated by the caller (api.cpp) before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace nvfp4 {
+
+hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
+                                  const uint16_t* rope, int64_t rstride,
+                                  const int64_t* slot_mapping, int64_t num_tokens,
+                                  uint8_t* cache, int64_t num_slots, const PageAddr& pa,
+                                  hipStream_t stream);
+
+hipError_t launch_dequantize_gather(const uint8_t* cache, int64_t num_slots, const PageAddr& pa,
+                                    const int32_t* slots, int64_t n, uint16_t* out,
+                                    hipStream_t stream);
+
+struct DecodeArgs {
+  const uint16_t* q;        // [rows, h_q, 576] bf16
+  const uint8_t* cache;
+  PageAddr pa;
+  int64_t num_slots;
+  const int32_t* indices;   // [rows, topk]
+  int32_t rows;             // batch * s_q
+  int32_t h_q;
+  int32_t topk;
+  const float* sink;        // [h_q] or null
+  float scale_log2;         // softmax_scale * log2(e)
+  uint16_t* out;            // [rows, h_q, 512] bf16
+  float* lse;               // [rows, h_q]
+  float* o_part;            // [splits, rows, h_q, 512] fp32 (splits > 1)
+  float* lse_part;          // [splits, rows, h_q]
+  int32_t splits;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
+                          int64_t rows, int32_t h_q, const float* sink, uint16_t* out,
+                          float* lse, hipStream_t stream);
+
+}  // namespace nvfp4
