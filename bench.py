@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the NVFP4 sparse-MLA path on one MI355X.
+
+One step = the whole hot path for one batch: quantize-append the step's new
+tokens (one per query row) into the paged NVFP4 cache, then the sparse decode
+(gather + dequant + QK + online softmax with sink + PV, split-KV merge inside
+the same kernel).  The headline workload is h_q 64 / batch 32 / top-k 2048;
+the h_q 16 MTP and h_q 128 varlen decode workloads and the 16384-token
+quantize-append are reported alongside.
+
+Inputs are resident in HBM before timing starts: each pool is filled with
+NVFP4 records by the HIP quantize-append, and the timed loop rotates over R
+independent index/query sets on that pool so successive steps do not simply
+re-read one step's records out of the 256 MB MALL.  Each step is captured once
+as HIP graphs (append, decode) and replayed; HIP events bracket every decode
+replay on the stream it runs on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FLOP_PER_TOKEN_HEAD = 2 * (576 + 512)
+HEADLINE = "decode_h64"
+METRIC = "sparse decode TFLOP/s + KV GB/s, h_q 16/64/128, topk 2048; % of roofline"
+DECODE_SRC = os.path.join(ROOT, "sparse_mla_decode_nvfp4_amd", "csrc", "decode.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--sets", type=int, default=8, help="index/query sets rotated over one pool")
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
+    p.add_argument("--only", default=None, help="run just this workload (profiling)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.dirname(DECODE_SRC))):
+        with open(os.path.join(os.path.dirname(DECODE_SRC), name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel code."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- decode
+def decode_accounting(sets, wl):
+    """Algorithmic flops and bytes per step (averaged over the sets)."""
+    fl, kv, uniq = [], [], []
+    for s in sets:
+        idx = s.indices
+        valid = (idx >= 0) & (idx < wl.num_slots)
+        nv = int(valid.sum())
+        fl.append(nv * FLOP_PER_TOKEN_HEAD * wl.h_q)
+        kv.append(nv * 352)
+        uniq.append(len(np.unique(idx[valid])) * 352)
+    rows = wl.batch * wl.s_q
+    other = (rows * wl.h_q * 576 * 2 + rows * wl.h_q * 512 * 2 + rows * wl.h_q * 4
+             + rows * wl.topk * 4 + wl.h_q * 4)
+    return dict(flops=float(np.mean(fl)), kv_bytes=float(np.mean(kv)),
+                unique_bytes=float(np.mean(uniq)) + other, other_bytes=other)
+
+
+def fill_pool(lib, W, wl, dev):
+    import torch
+    cache = lib.new_cache(wl.num_blocks, wl.block_size, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + wl.config_id)
+    chunk = 1 << 20
+    for start in range(0, wl.num_slots, chunk):
+        n = min(chunk, wl.num_slots - start)
+        lat, rope = W.latents_torch(wl.config_id, n, gen, dev)
+        sm = torch.arange(start, start + n, dtype=torch.int64, device=dev)
+        lib.quantize_append(lat, rope, sm, cache)
+        del lat, rope, sm
+    torch.cuda.synchronize()
+    return cache
+
+
+def bench_decode(lib, W, name, steps, warmup, nsets, use_graph, dev):
+    import torch
+    t_gen = time.time()
+    sets = [W.DECODE_WORKLOADS[name](rep=r, with_latents=False) for r in range(nsets)]
+    wl = sets[0]
+    log(f"{name}: {nsets} sets generated in {time.time() - t_gen:.1f}s; pool "
+        f"{wl.num_slots} slots = {wl.num_slots * 352 / 1e9:.2f} GB")
+    cache = fill_pool(lib, W, wl, dev)
+    rows = wl.batch * wl.s_q
+    splits = lib.plan(wl.batch, wl.s_q, wl.h_q, wl.topk)
+    ws_bytes = lib.workspace_size(wl.batch, wl.s_q, wl.h_q, wl.topk, splits)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.batch, wl.s_q, wl.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.batch, wl.s_q, wl.h_q), dtype=torch.float32, device=dev)
+    sink = torch.from_numpy(wl.sink).to(dev) if wl.sink is not None else None
+    new_slots = torch.from_numpy(wl.new_slots).to(dev)
+    inp = []
+    for r, s in enumerate(sets):
+        nl, nr = W.latents(wl.config_id, rows, rep=100 + r)
+        inp.append(dict(q=s.q.to(dev), idx=torch.from_numpy(s.indices).to(dev),
+                        lat=nl.to(dev), rope=nr.to(dev)))
+
+    def append(r):
+        lib.quantize_append(inp[r]["lat"], inp[r]["rope"], new_slots, cache)
+
+    def decode(r):
+        lib.sparse_decode(inp[r]["q"], cache, inp[r]["idx"], wl.softmax_scale, sink=sink,
+                          num_splits=splits, workspace=ws, out=out, lse=lse)
+
+    # eager reference outputs, then graphs checked against them
+    ref = []
+    for r in range(nsets):
+        append(r)
+        decode(r)
+        torch.cuda.synchronize()
+        ref.append(out.clone())
+    g_app, g_dec = [], []
+    if use_graph:
+        for r in range(nsets):
+            ga, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga):
+                append(r)
+            with torch.cuda.graph(gd):
+                decode(r)
+            g_app.append(ga)
+            g_dec.append(gd)
+        for rnd in range(2):
+            for r in range(nsets):
+                g_app[r].replay()
+                g_dec[r].replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out, ref[r]), f"{name}: graph replay {rnd} set {r} differs"
+        run_app = lambda r: g_app[r].replay()
+        run_dec = lambda r: g_dec[r].replay()
+    else:
+        run_app, run_dec = append, decode
+
+    for k in range(warmup):
+        run_app(k % nsets)
+        run_dec(k % nsets)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        r = k % nsets
+        run_app(r)
+        ev[k][0].record()
+        run_dec(r)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    acc = decode_accounting(sets, wl)
+    step_ms = (t1 - t0) * 1e3 / steps
+    dec_avg = float(dec_ms.mean())
+    res = dict(
+        workload=name, description=wl.description, rows=rows, h_q=wl.h_q, topk=wl.topk,
+        splits=splits, sets=nsets, ms_per_step=step_ms,
+        decode_ms_mean=dec_avg, decode_ms_median=float(np.median(dec_ms)),
+        decode_ms_min=float(dec_ms.min()),
+        flops_per_step=acc["flops"], kv_bytes_per_step=acc["kv_bytes"],
+        compulsory_bytes_per_step=acc["unique_bytes"],
+        step_tflops=acc["flops"] / (step_ms * 1e-3) / 1e12,
+        decode_tflops=acc["flops"] / (dec_avg * 1e-3) / 1e12,
+        decode_kv_gbps=acc["kv_bytes"] / (dec_avg * 1e-3) / 1e9,
+        decode_hbm_gbps=acc["unique_bytes"] / (dec_avg * 1e-3) / 1e9,
+    )
+    res["mfma_frac"] = res["decode_tflops"] / PEAK_BF16_TFLOPS
+    res["hbm_frac"] = res["decode_hbm_gbps"] / PEAK_HBM_GBS
+    intensity = acc["flops"] / acc["unique_bytes"]
+    res["bound"] = "mfma" if intensity > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    log(f"{name}: step {step_ms * 1e3:.1f} us, decode {dec_avg * 1e3:.1f} us (median "
+        f"{res['decode_ms_median'] * 1e3:.1f}), {res['decode_tflops']:.0f} TFLOP/s "
+        f"({100 * res['mfma_frac']:.1f}% MFMA), KV {res['decode_kv_gbps']:.0f} GB/s, "
+        f"compulsory {res['decode_hbm_gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
+        f"splits {splits}")
+    del cache, ws, inp, g_app, g_dec
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_append(lib, W, steps, warmup, dev):
+    import torch
+    wl = W.append_write()
+    cache = torch.from_numpy(wl.sentinel.reshape(wl.num_blocks, wl.block_size, 352)).to(dev)
+    lat, rope = wl.latent.to(dev), wl.rope.to(dev)
+    sm = torch.from_numpy(wl.slot_mapping).to(dev)
+    for _ in range(warmup):
+        lib.quantize_append(lat, rope, sm, cache)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record()
+        lib.quantize_append(lat, rope, sm, cache)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    mapped = int((wl.slot_mapping >= 0).sum())
+    nbytes = mapped * (512 * 2 + 64 * 2 + 352) + wl.num_tokens * 8
+    res = dict(workload="append_write", tokens=wl.num_tokens, mapped=mapped, ms=ms,
+               bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9,
+               tokens_per_s=mapped / (ms * 1e-3))
+    res["hbm_frac"] = res["gbps"] / PEAK_HBM_GBS
+    log(f"append_write: {ms * 1e3:.1f} us, {res['gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM)")
+    del cache
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------- cpu
+def cpu_baseline(W, name, budget_s=12.0):
+    """The oracle (numpy fp64) timed on this host: the step's quantize-append
+    of its new tokens plus the decode of a bounded sample of query rows."""
+    import torch
+    from oracle import attention as OA
+    from oracle import codec as OC
+    wl = W.DECODE_WORKLOADS[name](rep=0, with_latents=False)
+    rows = wl.batch * wl.s_q
+    idx = wl.indices.reshape(rows, wl.topk).astype(np.int64)
+    q = wl.q.reshape(rows, wl.h_q, 576).to(torch.float64).numpy()
+    nl, nr = W.latents(wl.config_id, rows, rep=100)
+    nl64, nr64 = nl.to(torch.float64).numpy(), nr.to(torch.float64).numpy()
+
+    def prepare(r):
+        ids = idx[r]
+        uniq = np.unique(ids[ids >= 0])
+        lat, rope = W.latents(wl.config_id, len(uniq), rep=200 + r)
+        recs = OC.quantize_records(lat.to(torch.float64).numpy(), rope.to(torch.float64).numpy())
+        local = np.where(ids >= 0, np.searchsorted(uniq, np.maximum(ids, 0)), -1)
+        return recs, local
+
+    sink = None if wl.sink is None else wl.sink.astype(np.float64)
+    t0 = time.perf_counter()
+    OC.quantize_records(nl64, nr64)                       # the step's append
+    t_app = time.perf_counter() - t0
+    done, t_dec, flops = 0, 0.0, 0.0
+    while done < rows and t_dec + t_app < budget_s:
+        recs, local = prepare(done)                       # cache contents: not timed
+        t0 = time.perf_counter()
+        OA.sparse_decode(q[done][None, None], recs, local[None, None], wl.softmax_scale, sink=sink)
+        t_dec += time.perf_counter() - t0
+        flops += int((local >= 0).sum()) * FLOP_PER_TOKEN_HEAD * wl.h_q
+        done += 1
+    cores = len(os.sched_getaffinity(0))
+    return dict(value=flops / (t_app + t_dec) / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{done} of {rows} query rows of {name} (decode, float64 numpy) plus the "
+                       f"step's {rows}-token quantize-append; {t_app + t_dec:.1f} s",
+                seconds=t_app + t_dec)
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+              "requested). See DESIGN.md for how the decode would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_mla_decode_nvfp4_amd as lib
+    from sparse_mla_decode_nvfp4_amd import workloads as W
+    lib.lib()                      # fails loudly when the HIP library is missing
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    use_graph = not args.no_graph
+
+    if args.only:
+        if args.only == "append_write":
+            res = bench_append(lib, W, args.steps, args.warmup, dev)
+        else:
+            res = bench_decode(lib, W, args.only, args.steps, args.warmup, args.sets, use_graph, dev)
+        print(json.dumps(res))
+        return
+
+    head = bench_decode(lib, W, args.workload, args.steps, args.warmup, args.sets, use_graph, dev)
+    extra = {}
+    if not args.no_extra:
+        for name in ("decode_h16_mtp", "decode_h128_varlen"):
+            if name != args.workload:
+                extra[name] = bench_decode(lib, W, name, max(20, args.steps // 2),
+                                           max(5, args.warmup // 2), args.sets, use_graph, dev)
+        extra["append_write"] = bench_append(lib, W, max(20, args.steps // 2),
+                                             max(5, args.warmup // 2), dev)
+    cpu = None if args.no_cpu else cpu_baseline(W, args.workload)
+
+    bound = head["bound"]
+    if bound == "mfma":
+        achieved, peak, unit = head["decode_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = head["decode_hbm_gbps"], PEAK_HBM_GBS, "GB/s"
+    line = {
+        "metric": METRIC,
+        "value": head["step_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": 32, "s_q": 1, "h_q": 64, "topk": 2048,
+                   "d_qk": 576, "d_v": 512, "record_bytes": 352, "block_size": 64,
+                   "invalid_frac": 0.05, "sink": True, "splits": head["splits"],
+                   "index_sets": args.sets, "graphs": use_graph},
+        "kv_gbps": head["kv_bytes_per_step"] / (head["ms_per_step"] * 1e-3) / 1e9,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": measured_traffic(args.workload),
+                     "kernel": "decode_stream16_kernel",
+                     "kernel_us_mean": head["decode_ms_mean"] * 1e3,
+                     "other_resource_frac": head["hbm_frac"] if bound == "mfma" else head["mfma_frac"]},
+        "cpu_baseline": cpu,
+        "workloads": {args.workload: head, **extra},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -136,6 +136,15 @@ int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q,
  * Workspace bytes a decode with num_splits partitions needs (0 when
  * num_splits == 1).  num_splits == 0 means "what the planner picks".
  * Returns 0 and sets the error on invalid arguments.
+ *
+ * The workspace holds the splits' partial O and LSE and one arrival counter
+ * per (query row, group of 16 heads); the last split to finish merges the
+ * partials inside the decode kernel.  The caller zero-fills a workspace
+ * before its first use with a given (batch, s_q, h_q, num_splits); every
+ * completed decode leaves the counters zero again, so further decodes of
+ * that shape reuse it without clearing (a different shape needs a fresh
+ * zero fill, since the counters move).  Decodes that may run concurrently
+ * need separate workspaces.
  */
 size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
                                               int32_t h_q, int32_t topk,
@@ -162,7 +171,7 @@ size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
  *              bytes (may be NULL when that size is 0); 256-byte aligned
  *   num_splits 0 = planner's choice, else 1..NVFP4_MLA_MAX_SPLITS
  * h_q must be a multiple of 16 (1..16 * 16), topk in [1, 65536].
- * When num_splits > 1 the decode also launches the combine.
+ * The whole decode, including the split-KV merge, is one kernel launch.
  */
 int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int64_t num_blocks, int32_t block_size,

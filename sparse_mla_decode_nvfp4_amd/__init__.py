@@ -163,6 +163,7 @@ def plan(batch, s_q, h_q, topk):
 
 
 def workspace_size(batch, s_q, h_q, topk, num_splits=0):
+    """Bytes of decode workspace; allocate it zero-filled (torch.zeros) once."""
     n = lib().nvfp4_mla_sparse_decode_workspace_size(batch, s_q, h_q, topk, num_splits)
     err = last_error()
     if err:
@@ -188,7 +189,8 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
         num_splits = plan(b, s, h, topk)
     need = workspace_size(b, s, h, topk, num_splits)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled once: the split-merge counters must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
     if lse is None:

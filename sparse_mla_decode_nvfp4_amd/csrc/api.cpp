@@ -142,11 +142,31 @@ int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
   return (int)want;
 }
 
-size_t workspace_bytes(int64_t rows, int32_t h_q, int32_t splits) {
-  if (splits <= 1) return 0;
+// Workspace layout for splits > 1 (each region 256-byte aligned):
+//   o_part   [splits, rows, h_q, 512] fp32
+//   lse_part [splits, rows, h_q] fp32
+//   counters [rows, h_q/16] uint32 -- zero on entry, left zero on exit
+struct WsLayout {
+  size_t o_off, lse_off, cnt_off, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int64_t rows, int32_t h_q, int32_t splits) {
+  WsLayout w{0, 0, 0, 0};
+  if (splits <= 1) return w;
   const size_t o = (size_t)splits * rows * h_q * NVFP4_MLA_V_DIM * sizeof(float);
-  const size_t o_al = (o + 255) & ~(size_t)255;
-  return o_al + (size_t)splits * rows * h_q * sizeof(float);
+  const size_t l = (size_t)splits * rows * h_q * sizeof(float);
+  const size_t c = (size_t)rows * (h_q / 16) * sizeof(uint32_t);
+  w.o_off = 0;
+  w.lse_off = align256(o);
+  w.cnt_off = w.lse_off + align256(l);
+  w.total = w.cnt_off + align256(c);
+  return w;
+}
+
+size_t workspace_bytes(int64_t rows, int32_t h_q, int32_t splits) {
+  return ws_layout(rows, h_q, splits).total;
 }
 
 }  // namespace
@@ -314,19 +334,15 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache, int64_t
   a.lse = lse;
   a.splits = splits;
   if (splits > 1) {
-    const size_t o = (size_t)splits * rows * h_q * NVFP4_MLA_V_DIM * sizeof(float);
-    a.o_part = static_cast<float*>(workspace);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o + 255) & ~(size_t)255));
+    const WsLayout w = ws_layout(rows, h_q, splits);
+    char* base = static_cast<char*>(workspace);
+    a.o_part = reinterpret_cast<float*>(base + w.o_off);
+    a.lse_part = reinterpret_cast<float*>(base + w.lse_off);
+    a.counters = reinterpret_cast<uint32_t*>(base + w.cnt_off);
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = nvfp4::launch_decode(a, st);
+  hipError_t e = nvfp4::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(NVFP4_MLA_ERR_HIP, "sparse_decode launch failed: %s", hipGetErrorString(e));
-  if (splits > 1) {
-    e = nvfp4::launch_combine(a.o_part, a.lse_part, splits, rows, h_q, attn_sink, a.out, lse, st);
-    if (e != hipSuccess)
-      return fail(NVFP4_MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
-  }
   return ok();
 }
 

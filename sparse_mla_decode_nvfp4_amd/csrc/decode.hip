@@ -26,6 +26,7 @@
 //     exceeds it by more than 2^8, so rescales are rare.
 #include <math.h>
 
+#include "combine_math.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -80,6 +81,8 @@ decode_stream16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t vtile[NW][16][kVRow];
   __shared__ float red_m[NW][16];
   __shared__ float red_l[NW][16];
+  __shared__ float sh_ms[16];
+  __shared__ float sh_lt[16];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -250,12 +253,8 @@ decode_stream16_kernel(DecodeArgs a) {
     red_l[wave][n] = l_tot;
   }
   __syncthreads();
-  // per-head global max and this wave's weight, for the heads of O's rows
-  float wfac[4];
-  float mstar_r[4], ltot_r[4];
-#pragma unroll
-  for (int r = 0; r < 4; r++) {
-    const int h = 4 * g + r;
+  if (threadIdx.x < 16) {              // per-head max and denominator over waves
+    const int h = threadIdx.x;
     float ms = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; w++) ms = fmaxf(ms, red_m[w][h]);
@@ -265,17 +264,21 @@ decode_stream16_kernel(DecodeArgs a) {
       const float mw = red_m[w][h];
       lt += (mw == -INFINITY) ? 0.f : exp2f(mw - ms) * red_l[w][h];
     }
-    const float mw = red_m[wave][h];
-    wfac[r] = (mw == -INFINITY) ? 0.f : exp2f(mw - ms);
-    mstar_r[r] = ms;
-    ltot_r[r] = lt;
+    sh_ms[h] = ms;
+    sh_lt[h] = lt;
   }
-  (void)mstar_r;
-  (void)ltot_r;
+  __syncthreads();
+  float wfac[4];                       // this wave's weight for O rows 4g+r
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const float mw = red_m[wave][4 * g + r];
+    wfac[r] = (mw == -INFINITY) ? 0.f : exp2f(mw - sh_ms[4 * g + r]);
+  }
   // the V tiles are reused as the reduction buffer: [NW][16 heads][256 dv] fp32
   float* redbuf = reinterpret_cast<float*>(&vtile[0][0][0]);
   static_assert(sizeof(vtile) >= NW * 16 * 256 * sizeof(float), "reduction buffer too small");
   const size_t orow_base = ((size_t)row * a.h_q + h0);
+  const size_t part_base = ((size_t)split * a.rows + row) * a.h_q + h0;
   for (int half = 0; half < 2; half++) {
     __syncthreads();
 #pragma unroll
@@ -286,7 +289,6 @@ decode_stream16_kernel(DecodeArgs a) {
         redbuf[(wave * 16 + 4 * g + r) * 256 + 16 * nbh + n] = acc_o[nb][r] * wfac[r];
     }
     __syncthreads();
-    // each thread finishes 16*256/(64*NW) output pairs
     for (int e2 = threadIdx.x; e2 < 16 * 128; e2 += 64 * NW) {
       const int h = e2 >> 7;
       const int dv2 = (e2 & 127) * 2;
@@ -296,15 +298,8 @@ decode_stream16_kernel(DecodeArgs a) {
         v0 += redbuf[(w * 16 + h) * 256 + dv2];
         v1 += redbuf[(w * 16 + h) * 256 + dv2 + 1];
       }
-      float ms = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; w++) ms = fmaxf(ms, red_m[w][h]);
-      float lt = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; w++) {
-        const float mw = red_m[w][h];
-        lt += (mw == -INFINITY) ? 0.f : exp2f(mw - ms) * red_l[w][h];
-      }
+      const float ms = sh_ms[h];
+      const float lt = sh_lt[h];
       const int dv = half * 256 + dv2;
       if (a.splits == 1) {
         float denom = lt;
@@ -315,16 +310,39 @@ decode_stream16_kernel(DecodeArgs a) {
         *reinterpret_cast<uint32_t*>(a.out + (orow_base + h) * kVDim + dv) = pk;
       } else {
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-        float* op = a.o_part + (((size_t)split * a.rows + row) * a.h_q + h0 + h) * kVDim + dv;
-        *reinterpret_cast<f32x2*>(op) = f32x2{v0 * inv, v1 * inv};
-      }
-      if (half == 0 && dv2 == 0) {
-        const float lse = lt > 0.f ? (ms + log2f(lt)) * 0.6931471805599453f : -INFINITY;
-        if (a.splits == 1) a.lse[orow_base + h] = lse;
-        else a.lse_part[((size_t)split * a.rows + row) * a.h_q + h0 + h] = lse;
+        *reinterpret_cast<f32x2*>(a.o_part + (part_base + h) * kVDim + dv) =
+            f32x2{v0 * inv, v1 * inv};
       }
     }
   }
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
+    const float lt = sh_lt[h];
+    const float lse = lt > 0.f ? (sh_ms[h] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+    if (a.splits == 1) a.lse[orow_base + h] = lse;
+    else a.lse_part[part_base + h] = lse;
+  }
+  if (a.splits == 1) return;
+
+  // ---- split-KV: the last split of this (row, head group) to finish merges
+  // all splits' partials.  Release the partials device-wide, count, and let
+  // the last arrival acquire them; it resets the counter for the next call.
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  uint32_t* counter = a.counters + (size_t)row * hgroups + hg;
+  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1u) == (uint32_t)(a.splits - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int64_t rh0 = (int64_t)row * a.h_q + h0;
+  const int64_t part_stride = (int64_t)a.rows * a.h_q;
+  for (int e = threadIdx.x; e < 16 * (kVDim / 4); e += 64 * NW) {
+    const int h = e / (kVDim / 4);
+    combine_chunk4(a.o_part, a.lse_part, a.splits, part_stride, rh0 + h, 4 * (e % (kVDim / 4)),
+                   a.sink != nullptr ? a.sink + h0 + h : nullptr, a.out, a.lse);
+  }
+  if (threadIdx.x == 0) *counter = 0u;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -34,6 +34,7 @@ struct DecodeArgs {
   float* lse;               // [rows, h_q]
   float* o_part;            // [splits, rows, h_q, 512] fp32 (splits > 1)
   float* lse_part;          // [splits, rows, h_q]
+  uint32_t* counters;       // [rows, h_q/16], zero on entry and on exit
   int32_t splits;
 };
 

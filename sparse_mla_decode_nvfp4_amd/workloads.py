@@ -56,6 +56,17 @@ def latents(config_id, n, rep=0):
     return _bf16(nope), _bf16(rope)
 
 
+def latents_torch(config_id, n, generator, device):
+    """Same distributions as latents(), drawn with a seeded torch generator
+    on `device` (used to fill whole multi-GB pools quickly)."""
+    cs = torch.from_numpy(channel_scales(config_id)).to(device=device, dtype=torch.float32)
+    nope = torch.randn((n, NOPE_DIM), generator=generator, device=device) * cs
+    outlier = torch.rand((n, NOPE_DIM), generator=generator, device=device) < 0.01
+    nope = torch.where(outlier, nope * 20.0, nope)
+    rope = torch.randn((n, ROPE_DIM), generator=generator, device=device)
+    return nope.to(torch.bfloat16), rope.to(torch.bfloat16)
+
+
 @dataclass
 class DecodeWorkload:
     """One decode step's inputs.
@@ -80,8 +91,8 @@ class DecodeWorkload:
     indices: np.ndarray                  # int32 [B, S_q, topk]
     sink: Optional[np.ndarray]           # float32 [H] or None
     slots: np.ndarray                    # int64 [n] sorted distinct
-    latent: torch.Tensor                 # bf16 [n, 512]
-    rope: torch.Tensor                   # bf16 [n, 64]
+    latent: Optional[torch.Tensor]       # bf16 [n, 512] (None: not drawn)
+    rope: Optional[torch.Tensor]         # bf16 [n, 64]
     new_slots: np.ndarray                # int64 [B * S_q]
     description: str = ""
     extra: dict = field(default_factory=dict)
@@ -112,13 +123,16 @@ def _page_table(r, pages_per_seq):
 
 
 def _finish(name, cid, batch, s_q, h_q, topk, bs, num_blocks, scale, idx,
-            new_slots, with_sink, description, rep=0, extra=None):
+            new_slots, with_sink, description, rep=0, extra=None, with_latents=True):
     q = _bf16(_rng(cid, 3, rep).standard_normal((batch, s_q, h_q, QK_DIM)))
-    sink = (_rng(cid, 5, rep).standard_normal(h_q).astype(np.float32)
+    sink = (_rng(cid, 5, 0).standard_normal(h_q).astype(np.float32)
             if with_sink else None)
     used = np.concatenate([idx[idx >= 0].astype(np.int64), new_slots])
     slots = np.unique(used)
-    latent, rope = latents(cid, len(slots), rep)
+    if with_latents:
+        latent, rope = latents(cid, len(slots), rep)
+    else:
+        latent = rope = None
     return DecodeWorkload(name, cid, batch, s_q, h_q, topk, bs, num_blocks,
                           float(np.float32(scale)), q, idx.astype(np.int32),
                           sink, slots, latent, rope, new_slots.astype(np.int64),
@@ -130,7 +144,7 @@ def tiny(rep=0):
     filled entirely, 64 distinct random indices, no invalid entries, no sink,
     scale 1/sqrt(576).  The step's new token is the one at position 255."""
     cid, bs = 0, 64
-    tables, total = _page_table(_rng(cid, 6, rep), [4])
+    tables, total = _page_table(_rng(cid, 6, 0), [4])
     pos = _rng(cid, 4, rep).choice(256, size=64, replace=False)
     idx = (tables[0][pos // bs] * bs + pos % bs).reshape(1, 1, 64)
     new_slot = np.array([tables[0][255 // bs] * bs + 255 % bs])
@@ -143,11 +157,11 @@ def tiny(rep=0):
     return wl
 
 
-def decode_h64(rep=0, batch=32):
+def decode_h64(rep=0, batch=32, with_latents=True):
     """B 32, s_q 1, 64 heads, 32768 tokens per sequence in 64-token pages,
     random page table, 2048 distinct positions per query, 5 % invalid, sink."""
     cid, bs, seq, topk = 1, 64, 32768, 2048
-    tables, total = _page_table(_rng(cid, 6, rep), [seq // bs] * batch)
+    tables, total = _page_table(_rng(cid, 6, 0), [seq // bs] * batch)
     r4 = _rng(cid, 4, rep)
     idx = np.empty((batch, 1, topk), dtype=np.int64)
     new_slots = np.empty(batch, dtype=np.int64)
@@ -160,14 +174,14 @@ def decode_h64(rep=0, batch=32):
     return _finish("decode_h64", cid, batch, 1, 64, topk, bs, total,
                    1.0 / 24.0, idx, new_slots, True,
                    f"h_q 64: B{batch} S_q1, 32768-token contexts, topk 2048, "
-                   "5% invalid, sink", rep)
+                   "5% invalid, sink", rep, with_latents=with_latents)
 
 
-def decode_h128_varlen(rep=0, batch=64):
+def decode_h128_varlen(rep=0, batch=64, with_latents=True):
     """B 64, s_q 1, 128 heads, context length ~ U[4096, 131072], 64-token
     pages, topk = min(2048, len) distinct positions, 2 % invalid, sink."""
     cid, bs, topk = 2, 64, 2048
-    r6 = _rng(cid, 6, rep)
+    r6 = _rng(cid, 6, 0)
     lens = r6.integers(4096, 131072, endpoint=True, size=batch)
     pages = [int(-(-int(n) // bs)) for n in lens]
     tables, total = _page_table(r6, pages)
@@ -188,17 +202,17 @@ def decode_h128_varlen(rep=0, batch=64):
                    1.0 / 24.0, idx, new_slots, True,
                    f"h_q 128 varlen: B{batch} S_q1, lengths U[4096,131072], "
                    "topk 2048, 2% invalid, sink", rep,
-                   extra={"lengths": lens})
+                   extra={"lengths": lens}, with_latents=with_latents)
 
 
-def decode_h16_mtp(rep=0, batch=256):
+def decode_h16_mtp(rep=0, batch=256, with_latents=True):
     """B 256, s_q 2 (MTP), 16 heads, 65536-token contexts, 64-token pages.
     Query j sits at position L-2+j; its 640 indices are the 128-token window
     ending at that position followed by 512 distinct positions drawn from the
     older history; 3 % invalid; sink."""
     cid, bs, seq, s_q, win, extra_k = 4, 64, 65536, 2, 128, 512
     topk = win + extra_k
-    tables, total = _page_table(_rng(cid, 6, rep), [seq // bs] * batch)
+    tables, total = _page_table(_rng(cid, 6, 0), [seq // bs] * batch)
     r4 = _rng(cid, 4, rep)
     idx = np.empty((batch, s_q, topk), dtype=np.int64)
     new_slots = np.empty(batch * s_q, dtype=np.int64)
@@ -215,7 +229,8 @@ def decode_h16_mtp(rep=0, batch=256):
     return _finish("decode_h16_mtp", cid, batch, s_q, 16, topk, bs, total,
                    1.0 / 24.0, idx, new_slots, True,
                    f"h_q 16 MTP: B{batch} S_q2, 65536-token contexts, topk 640 "
-                   "(128 window + 512 history), 3% invalid, sink", rep)
+                   "(128 window + 512 history), 3% invalid, sink", rep,
+                   with_latents=with_latents)
 
 
 @dataclass
