@@ -48,8 +48,13 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graphs")
+    p.add_argument("--graph", action="store_true",
+                   help="time HIP-graph replays instead of eager launches (graphs are always "
+                        "captured and checked against the eager results)")
     p.add_argument("--only", default=None, help="run just this workload (profiling)")
+    p.add_argument("--splits", type=int, default=0, help="override the planner's split count")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -113,7 +118,7 @@ def fill_pool(lib, W, wl, dev):
     return cache
 
 
-def bench_decode(lib, W, name, steps, warmup, nsets, use_graph, dev):
+def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_splits=0):
     import torch
     t_gen = time.time()
     sets = [W.DECODE_WORKLOADS[name](rep=r, with_latents=False) for r in range(nsets)]
@@ -122,7 +127,7 @@ def bench_decode(lib, W, name, steps, warmup, nsets, use_graph, dev):
         f"{wl.num_slots} slots = {wl.num_slots * 352 / 1e9:.2f} GB")
     cache = fill_pool(lib, W, wl, dev)
     rows = wl.batch * wl.s_q
-    splits = lib.plan(wl.batch, wl.s_q, wl.h_q, wl.topk)
+    splits = force_splits or lib.plan(wl.batch, wl.s_q, wl.h_q, wl.topk)
     ws_bytes = lib.workspace_size(wl.batch, wl.s_q, wl.h_q, wl.topk, splits)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((wl.batch, wl.s_q, wl.h_q, 512), dtype=torch.bfloat16, device=dev)
@@ -149,8 +154,10 @@ def bench_decode(lib, W, name, steps, warmup, nsets, use_graph, dev):
         decode(r)
         torch.cuda.synchronize()
         ref.append(out.clone())
+    # every call is capture-safe: capture each step's append and decode as HIP
+    # graphs and check that replays reproduce the eager results bit for bit
     g_app, g_dec = [], []
-    if use_graph:
+    if True:
         for r in range(nsets):
             ga, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
             with torch.cuda.graph(ga):
@@ -165,6 +172,7 @@ def bench_decode(lib, W, name, steps, warmup, nsets, use_graph, dev):
                 g_dec[r].replay()
                 torch.cuda.synchronize()
                 assert torch.equal(out, ref[r]), f"{name}: graph replay {rnd} set {r} differs"
+    if time_graph:
         run_app = lambda r: g_app[r].replay()
         run_dec = lambda r: g_dec[r].replay()
     else:
@@ -191,6 +199,8 @@ def bench_decode(lib, W, name, steps, warmup, nsets, use_graph, dev):
     dec_avg = float(dec_ms.mean())
     res = dict(
         workload=name, description=wl.description, rows=rows, h_q=wl.h_q, topk=wl.topk,
+        kernel=("decode_hsplit_kernel" + (" + combine_kernel" if splits > 1 else "")
+                if wl.h_q == 64 else "decode_tile16_kernel"),
         splits=splits, sets=nsets, ms_per_step=step_ms,
         decode_ms_mean=dec_avg, decode_ms_median=float(np.median(dec_ms)),
         decode_ms_min=float(dec_ms.min()),
@@ -293,18 +303,29 @@ def main():
               "requested). See DESIGN.md for how the decode would shard.", file=sys.stderr)
         sys.exit(2)
     import torch
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of its dispatches
+        # give the counters' bytes per real byte moved
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 1 << 30, "dispatches": 3}))
+        return
     import sparse_mla_decode_nvfp4_amd as lib
     from sparse_mla_decode_nvfp4_amd import workloads as W
     lib.lib()                      # fails loudly when the HIP library is missing
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    use_graph = not args.no_graph
+    use_graph = args.graph
 
     if args.only:
         if args.only == "append_write":
             res = bench_append(lib, W, args.steps, args.warmup, dev)
         else:
-            res = bench_decode(lib, W, args.only, args.steps, args.warmup, args.sets, use_graph, dev)
+            res = bench_decode(lib, W, args.only, args.steps, args.warmup, args.sets, use_graph, dev,
+                               args.splits)
         print(json.dumps(res))
         return
 
@@ -340,11 +361,11 @@ def main():
         "config": {"workload": args.workload, "batch": 32, "s_q": 1, "h_q": 64, "topk": 2048,
                    "d_qk": 576, "d_v": 512, "record_bytes": 352, "block_size": 64,
                    "invalid_frac": 0.05, "sink": True, "splits": head["splits"],
-                   "index_sets": args.sets, "graphs": use_graph},
+                   "index_sets": args.sets, "timed_launches": "graph" if use_graph else "eager"},
         "kv_gbps": head["kv_bytes_per_step"] / (head["ms_per_step"] * 1e-3) / 1e9,
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
-                     "kernel": "decode_stream16_kernel",
+                     "kernel": head["kernel"],
                      "kernel_us_mean": head["decode_ms_mean"] * 1e3,
                      "other_resource_frac": head["hbm_frac"] if bound == "mfma" else head["mfma_frac"]},
         "cpu_baseline": cpu,

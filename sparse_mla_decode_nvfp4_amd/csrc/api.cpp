@@ -128,14 +128,18 @@ int check_decode_shape(int32_t batch, int32_t s_q, int32_t h_q, int32_t topk) {
   return NVFP4_MLA_OK;
 }
 
-// Deterministic split choice: enough workgroups for two per CU, each split
-// keeping at least four 16-token blocks per wave-set.
+// Deterministic split choice.  The head-split kernel (h_q a multiple of 64)
+// runs one 144 KB-LDS workgroup per CU and keeps at least two 64-token tiles
+// per split; the 16-head tile kernel runs two workgroups per CU and keeps at
+// least one tile per split.
 int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
-  const int64_t wgs = (int64_t)rows * (h_q / 16);
-  const int nblk = (topk + 15) / 16;
+  const bool hsplit = nvfp4::decode_uses_hsplit(h_q);
+  const int64_t wgs = (int64_t)rows * (hsplit ? h_q / 64 : h_q / 16);
+  const int ntiles = (topk + 63) / 64;
   if (wgs == 0) return 1;
-  int64_t want = (2 * (int64_t)cus + wgs - 1) / wgs;
-  const int64_t max_by_work = nblk / 4 > 0 ? nblk / 4 : 1;
+  const int64_t per_cu = hsplit ? 1 : 2;
+  int64_t want = (per_cu * (int64_t)cus + wgs - 1) / wgs;
+  const int64_t max_by_work = hsplit ? (ntiles / 2 > 0 ? ntiles / 2 : 1) : ntiles;
   if (want > max_by_work) want = max_by_work;
   if (want > NVFP4_MLA_MAX_SPLITS) want = NVFP4_MLA_MAX_SPLITS;
   if (want < 1) want = 1;
