@@ -11,9 +11,10 @@ quantize-append are reported alongside.
 Inputs are resident in HBM before timing starts: each pool is filled with
 NVFP4 records by the HIP quantize-append, and the timed loop rotates over R
 independent index/query sets on that pool so successive steps do not simply
-re-read one step's records out of the 256 MB MALL.  Each step is captured once
-as HIP graphs (append, decode) and replayed; HIP events bracket every decode
-replay on the stream it runs on.
+re-read one step's records out of the 256 MB MALL.  Steps are launched
+eagerly (--graph times HIP-graph replays instead; the graphs are always
+captured and checked against the eager results); HIP events bracket every
+decode on the stream it runs on.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -199,8 +200,7 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     dec_avg = float(dec_ms.mean())
     res = dict(
         workload=name, description=wl.description, rows=rows, h_q=wl.h_q, topk=wl.topk,
-        kernel=("decode_hsplit_kernel" + (" + combine_kernel" if splits > 1 else "")
-                if wl.h_q == 64 else "decode_tile16_kernel"),
+        kernel="decode_w32_kernel" if wl.h_q % 32 == 0 else "decode_tile16_kernel",
         splits=splits, sets=nsets, ms_per_step=step_ms,
         decode_ms_mean=dec_avg, decode_ms_median=float(np.median(dec_ms)),
         decode_ms_min=float(dec_ms.min()),
@@ -356,7 +356,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16" if head["kernel"] == "decode_w32_kernel" else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": 32, "s_q": 1, "h_q": 64, "topk": 2048,
                    "d_qk": 576, "d_v": 512, "record_bytes": 352, "block_size": 64,

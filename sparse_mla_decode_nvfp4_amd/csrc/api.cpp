@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -128,18 +129,19 @@ int check_decode_shape(int32_t batch, int32_t s_q, int32_t h_q, int32_t topk) {
   return NVFP4_MLA_OK;
 }
 
-// Deterministic split choice.  The head-split kernel (h_q a multiple of 64)
-// runs one 144 KB-LDS workgroup per CU and keeps at least two 64-token tiles
-// per split; the 16-head tile kernel runs two workgroups per CU and keeps at
-// least one tile per split.
+// Deterministic split choice: enough splits to give every CU work, no more
+// than the top-k list can feed.  The 32-head-group kernel runs one four-wave
+// workgroup per (row, 32 heads, split), one per CU, each of its two token
+// streams with at least one 32-token chunk; the 16-head tile kernel runs one
+// workgroup per (row, 16 heads, split), two per CU, at least one 64-token
+// tile each.
 int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
-  const bool hsplit = nvfp4::decode_uses_hsplit(h_q);
-  const int64_t wgs = (int64_t)rows * (hsplit ? h_q / 64 : h_q / 16);
-  const int ntiles = (topk + 63) / 64;
+  const bool w32 = nvfp4::decode_uses_w32(h_q);
+  const int64_t wgs = (int64_t)rows * (w32 ? h_q / 32 : h_q / 16);
   if (wgs == 0) return 1;
-  const int64_t per_cu = hsplit ? 1 : 2;
+  const int64_t per_cu = w32 ? 1 : 2;
   int64_t want = (per_cu * (int64_t)cus + wgs - 1) / wgs;
-  const int64_t max_by_work = hsplit ? (ntiles / 2 > 0 ? ntiles / 2 : 1) : ntiles;
+  const int64_t max_by_work = w32 ? std::max<int64_t>(1, ((topk + 31) / 32) / 2) : (topk + 63) / 64;
   if (want > max_by_work) want = max_by_work;
   if (want > NVFP4_MLA_MAX_SPLITS) want = NVFP4_MLA_MAX_SPLITS;
   if (want < 1) want = 1;

@@ -375,20 +375,11 @@ decode_tile16_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) *counter = 0u;
 }
 
-// Kernel choice by measurement on MI355X: the head-split kernel (each token
-// dequantized once for 64 heads) is faster at h_q = 64; at h_q = 128 the
-// 16-head tile kernel, whose two workgroups per CU hide latency better, is
-// faster despite dequantizing each token once per head group.
-bool decode_uses_hsplit(int32_t h_q) { return h_q == 64; }
+bool decode_uses_w32(int32_t h_q) { return h_q % 32 == 0; }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  if (decode_uses_hsplit(a.h_q)) {
-    hipError_t e = launch_decode_hsplit(a, stream);
-    if (e != hipSuccess || a.splits == 1) return e;
-    return launch_combine(a.o_part, a.lse_part, a.splits, a.rows, a.h_q, a.sink, a.out, a.lse,
-                          stream);
-  }
+  if (decode_uses_w32(a.h_q)) return launch_decode_w32(a, stream);
   const int grid = a.rows * (a.h_q / 16) * a.splits;
   hipLaunchKernelGGL((decode_tile16_kernel<true>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();

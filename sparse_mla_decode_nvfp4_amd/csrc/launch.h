@@ -38,12 +38,12 @@ struct DecodeArgs {
   int32_t splits;
 };
 
-// Decode launch: decode_uses_hsplit(h_q) selects the 64-head head-split
-// kernel (plus the combine kernel when split), otherwise the 16-head tile
-// kernel runs (with its in-kernel split merge).
+// Decode launch: head counts that are multiples of 32 run the 32-head-group
+// kernel (decode_w32.hip), others the 16-head tile kernel (decode.hip); both
+// merge split-KV partials in-kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_hsplit(const DecodeArgs& a, hipStream_t stream);
-bool decode_uses_hsplit(int32_t h_q);
+hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream);
+bool decode_uses_w32(int32_t h_q);
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
                           int64_t rows, int32_t h_q, const float* sink, uint16_t* out,

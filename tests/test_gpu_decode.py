@@ -72,8 +72,10 @@ def test_no_sink_duplicates_out_of_range_and_odd_pages(lib):
     assert_decode_close(o, lse, o_ref, l_ref, "dup/oob/bs48")
 
 
-def test_empty_rows_single_token_and_zero_query(lib):
-    recs, q, idx, sink, nb, bs = small_case(9, 4, 1, 16, 40, p_inval=0.0)
+@pytest.mark.parametrize("h", [16, 32, 64])
+def test_empty_rows_single_token_and_zero_query(lib, h):
+    note(f"edge rows h={h}")
+    recs, q, idx, sink, nb, bs = small_case(9, 4, 1, h, 40, p_inval=0.0)
     idx[0, 0, :] = -1                     # a row with no valid index
     idx[1, 0, :] = -1
     idx[1, 0, 13] = 77                    # exactly one valid token
@@ -86,7 +88,18 @@ def test_empty_rows_single_token_and_zero_query(lib):
     # no sink: a single valid token returns its value row exactly (weight 1)
     o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, None, nb, bs, 1)
     v = torch.from_numpy(OC.dequantize_records(recs[77:78])[0, :512]).to(torch.bfloat16)
-    assert torch.equal(o[1, 0].cpu(), v[None].expand(16, 512))
+    assert torch.equal(o[1, 0].cpu(), v[None].expand(h, 512))
+
+
+@pytest.mark.parametrize("h,splits", [(16, 1), (32, 1), (64, 3)])
+def test_large_scores_raise_the_running_max(lib, h, splits):
+    # scores spread over tens of log2 units: the online max is raised (and
+    # the accumulators rescaled) many times along the index list
+    note(f"large scores h={h} splits={splits}")
+    recs, q, idx, sink, nb, bs = small_case(31, 2, 1, h, 900)
+    q = (q.float() * 24.0).to(torch.bfloat16)
+    o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
+    assert_decode_close(o, lse, o_ref, l_ref, f"large scores h{h}")
 
 
 def test_split_counts_agree(lib):
