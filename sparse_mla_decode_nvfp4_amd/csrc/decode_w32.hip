@@ -21,20 +21,20 @@
 //     (bit-identical sums), run the same online softmax and feed P, already in
 //     the PV operand layout, to O += P V (32x32x16 MFMAs) on their own V half,
 //     read transposed from a wave-private XOR-swizzled LDS tile;
-//   * Q is converted to fp16 once per wave with a per-head power-of-two
-//     scale (the two halves agree on it through LDS), folded into the softmax
-//     scale (exact for every bf16 element within 2^31 of its head's largest);
+//   * Q is converted to fp16 once per wave (kept in registers) with a
+//     per-head power-of-two scale (the two halves agree on it through LDS),
+//     folded into the softmax scale (exact for every bf16 element within 2^31
+//     of its head's largest);
 //   * P is rounded to fp16 for the PV product (relative error 2^-12); the
 //     running max is raised lazily, only when a score exceeds it by more than
 //     2^15 (so P stays in fp16 range and rescales of O are rare);
 //   * the two pairs merge their states through LDS at the end, and each wave
 //     writes a quarter of the output dims.
 // Split partials (sink-free O normalised within the split, LSE) are merged by
-// the last split to finish; all workgroups of a row share an XCD when the row
-// count allows (records and partials stay in that XCD's L2).
+// the combine kernel launched right after; all workgroups of a row share an
+// XCD when the row count allows (the row's records stay in that XCD's L2).
 #include <math.h>
 
-#include "combine_math.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -98,62 +98,20 @@ __device__ __forceinline__ int vswz_p(int t) { return ((t & 3) << 2) | ((t >> 2)
 // Row (token or head) of element r of a 32x32 accumulator in lane half kg.
 __device__ __forceinline__ int acc_row(int r, int kg) { return 8 * (r >> 2) + 4 * kg + (r & 3); }
 
+// Value of lane l ^ 32 combined with this lane's, through one VALU lane swap.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int V>
 struct IntC {
   static constexpr int value = V;
 };
-
-// LSE-weighted merge of the split partials of 32 heads (rows rh0..rh0+31 of
-// the [rows*h_q] partial arrays), one (head, 64-dim slice) per thread, every
-// load of a split issued before any of its products (same formulas as
-// combine_chunk4).
-__device__ __forceinline__ void merge_splits_w32(const DecodeArgs& a, int64_t rh0, int h0) {
-  const int h = threadIdx.x >> 3;
-  const int d0 = 64 * (threadIdx.x & 7);
-  const int64_t rh = rh0 + h;
-  const int64_t stride = (int64_t)a.rows * a.h_q;
-  const float* __restrict__ lp = a.lse_part + rh;
-  float m = -INFINITY;
-  for (int sp = 0; sp < a.splits; sp++) m = fmaxf(m, lp[sp * stride]);
-  uint16_t* orow = a.out + rh * kVDim + d0;
-  if (m == -INFINITY) {
-#pragma unroll
-    for (int c = 0; c < 8; c++) *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{0u, 0u, 0u, 0u};
-    if (d0 == 0) a.lse[rh] = -INFINITY;
-    return;
-  }
-  f32x4 acc[16];
-#pragma unroll
-  for (int c = 0; c < 16; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  for (int sp = 0; sp < a.splits; sp++) {
-    const float ls = lp[sp * stride];
-    const float w = (ls == -INFINITY) ? 0.f : expf(ls - m);
-    tot += w;
-    const f32x4* __restrict__ src = reinterpret_cast<const f32x4*>(a.o_part + (sp * stride + rh) * kVDim + d0);
-    f32x4 v[16];
-#pragma unroll
-    for (int c = 0; c < 16; c++) v[c] = src[c];
-#pragma unroll
-    for (int c = 0; c < 16; c++) acc[c] += w * v[c];
-  }
-  const float lse_v = m + logf(tot);
-  float inv = 1.0f / tot;
-  if (a.sink != nullptr) inv /= (1.0f + expf(a.sink[h0 + h] - lse_v));
-#pragma unroll
-  for (int c = 0; c < 8; c++) {
-    uint32_t wv[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const float x0 = acc[2 * c + (k >> 1)][2 * (k & 1)] * inv;
-      const float x1 = acc[2 * c + (k >> 1)][2 * (k & 1) + 1] * inv;
-      wv[k] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
-    }
-    *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-  }
-  if (d0 == 0) a.lse[rh] = lse_v;
-}
 
 }  // namespace
 
@@ -171,9 +129,6 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
   lds_u8* const vt_all = (lds_u8*)smem_p;                      // 4 x 16 KB V tiles
   lds_u8* const xs_all = vt_all + 4 * kVTileP;                 // [2 bufs][4 waves] partial S^T
   lds_f32* const stat = (lds_f32*)(xs_all + 2 * 4 * kXsBytes); // [4 waves][2][32]
-  __attribute__((address_space(3))) int* const s_last =
-      (__attribute__((address_space(3))) int*)(stat + 4 * 2 * 32);
-  lds_u8* const qlds = (lds_u8*)(s_last + 8);                         // [2 halves][18][64] x 16 B
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -263,11 +218,6 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
       }
       qB[j] = v;
     }
-    if (pr == 0) {
-#pragma unroll
-      for (int j = 0; j < 18; j++)
-        *reinterpret_cast<lds_f16x8*>(qlds + ((hf * 18 + j) * 64 + lane) * 16) = qB[j];
-    }
   }
 
   f32x16 acc_o[8];
@@ -335,8 +285,13 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
     const uint8_t* const rec_next = rec_of(nxt);
     const u32x4 rope = cur.rope;
     load_tail(cur, rec_next, hf, kg);      // scales and RoPE of the next chunk
+    // two accumulators (even / odd k-steps) halve the dependent MFMA chain
+    f32x16 sacc1;
 #pragma unroll
-    for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+    for (int r = 0; r < 16; r++) {
+      sacc[r] = 0.f;
+      sacc1[r] = 0.f;
+    }
 #pragma unroll
     for (int m = 0; m < 8; m++) {
       const uint32_t sw = (m & 1) ? so : se;
@@ -354,8 +309,8 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
         const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 3) * F;
         const f16x8 k = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
         *reinterpret_cast<lds_f16x8*>((lds_u8*)(size_t)wb[m & 3][h] + 256 * (m >> 2)) = k;
-        const f16x8 qv = *reinterpret_cast<const lds_f16x8*>(qlds + ((hf * 18 + 2 * m + h) * 64 + lane) * 16);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qv, sacc, 0, 0, 0);
+        if (h == 0) sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qB[2 * m], sacc, 0, 0, 0);
+        else sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qB[2 * m + 1], sacc1, 0, 0, 0);
       }
       cur.nope[m] = load_nope(rec_next, m, hf, kg);
     }
@@ -366,9 +321,10 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
       const f16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rope[2 * h + 1], 1.0f, false);
       const f16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rope[2 * h + 1], 1.0f, true);
       const f16x8 k = f16x8{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-      const f16x8 qv = *reinterpret_cast<const lds_f16x8*>(qlds + ((hf * 18 + 16 + h) * 64 + lane) * 16);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qv, sacc, 0, 0, 0);
+      if (h == 0) sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qB[16], sacc, 0, 0, 0);
+      else sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qB[17], sacc1, 0, 0, 0);
     }
+    sacc += sacc1;
     cur_idx = nxt;
     nxt_raw = nxt2_raw;
     lds_u8* const xs = xs_all + (pos & 1) * 4 * kXsBytes;
@@ -403,7 +359,7 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
       s[r] = __builtin_amdgcn_inverse_ballot_w64(keep) ? s[r] * qscale : -INFINITY;
       bm = fmaxf(bm, s[r]);
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = max_halves(bm);
     const bool need = bm > m_use + kLazyP;
     if (__any(need)) {
       const float m_new = need ? bm : m_use;
@@ -482,7 +438,7 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
   }
 
   // ---- merge the two pairs (same heads and output dims, disjoint tokens)
-  l_part += __shfl_xor(l_part, 32);
+  l_part = sum_halves(l_part);
   if (kg == 0) {
     stat[(wave * 2 + 0) * 32 + tl] = m_use;
     stat[(wave * 2 + 1) * 32 + tl] = l_part;
@@ -539,14 +495,13 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
   // ---- normalise and write this wave's quarter of the output dims
   const bool single = a.splits == 1;
   float inv[16];
+  {
+    // one denominator per head (lane tl holds head tl), then to the O layout
+    float denom = Lh;
+    if (single && a.sink != nullptr && Lh > 0.f) denom += __builtin_amdgcn_exp2f(a.sink[h0 + tl] * kLog2eP - Mh);
+    const float invh = Lh > 0.f ? 1.0f / denom : 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int hr = acc_row(r, kg);
-    const float M = __shfl(Mh, hr);
-    const float L = __shfl(Lh, hr);
-    float denom = L;
-    if (single && a.sink != nullptr && L > 0.f) denom += __builtin_amdgcn_exp2f(a.sink[h0 + hr] * kLog2eP - M);
-    inv[r] = L > 0.f ? 1.0f / denom : 0.f;
+    for (int r = 0; r < 16; r++) inv[r] = __shfl(invh, acc_row(r, kg));
   }
   const size_t orow = (size_t)row * a.h_q + h0;
   const size_t prow = ((size_t)split * a.rows + row) * a.h_q + h0;
@@ -573,26 +528,9 @@ __global__ void __launch_bounds__(256, 1) decode_w32_kernel(DecodeArgs a) {
     if (single) a.lse[orow + tl] = lse;
     else a.lse_part[prow + tl] = lse;
   }
-  if (single) return;
-
-  // ---- split-KV: the last split of this unit to finish merges all splits.
-  // The barrier completes every wave's partial stores; one thread releases
-  // them device-wide, counts, and the last arrival acquires the others'.
-  __syncthreads();
-  uint32_t* counter = a.counters + (size_t)row * (a.h_q >> 4) + hgrp;
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const bool last = atomicAdd(counter, 1u) == (uint32_t)(a.splits - 1);
-    if (last) __threadfence();
-    *s_last = last;
-  }
-  __syncthreads();
-  if (!*s_last) return;
-  merge_splits_w32(a, (int64_t)row * a.h_q + h0, h0);
-  if (threadIdx.x == 0) *counter = 0u;
 }
 
-size_t decode_w32_lds_bytes() { return 4 * kVTileP + 2 * 4 * kXsBytes + 4 * 2 * 32 * sizeof(float) + 32 + 2 * 18 * 64 * 16; }
+size_t decode_w32_lds_bytes() { return 4 * kVTileP + 2 * 4 * kXsBytes + 4 * 2 * 32 * sizeof(float); }
 
 hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.rows * (a.h_q / 32) * a.splits;
@@ -605,7 +543,12 @@ hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   hipLaunchKernelGGL(decode_w32_kernel, dim3(grid), dim3(256), lds, stream, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  // split partials are merged by the combine kernel: the launch boundary
+  // makes them visible across XCDs without device-scope fences (on a
+  // multi-XCD part those write back and invalidate L2)
+  return launch_combine(a.o_part, a.lse_part, a.splits, a.rows, a.h_q, a.sink, a.out, a.lse, stream);
 }
 
 }  // namespace nvfp4
