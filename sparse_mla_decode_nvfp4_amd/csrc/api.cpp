@@ -141,7 +141,8 @@ int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
   if (wgs == 0) return 1;
   const int64_t per_cu = w32 ? 1 : 2;
   int64_t want = (per_cu * (int64_t)cus + wgs - 1) / wgs;
-  const int64_t max_by_work = w32 ? std::max<int64_t>(1, ((topk + 31) / 32) / 2) : (topk + 63) / 64;
+  // w32: 16-token chunks over four token streams; keep at least two steps per split
+  const int64_t max_by_work = w32 ? std::max<int64_t>(1, ((topk + 15) / 16) / 8) : (topk + 63) / 64;
   if (want > max_by_work) want = max_by_work;
   if (want > NVFP4_MLA_MAX_SPLITS) want = NVFP4_MLA_MAX_SPLITS;
   if (want < 1) want = 1;

@@ -39,8 +39,9 @@ struct DecodeArgs {
 };
 
 // Decode launch: head counts that are multiples of 32 run the 32-head-group
-// kernel (decode_w32.hip), others the 16-head tile kernel (decode.hip); both
-// merge split-KV partials in-kernel.
+// kernel (decode_w32.hip), whose split-KV partials the combine kernel merges
+// right after; other head counts run the 16-head tile kernel (decode.hip),
+// which merges its partials in-kernel (last-arriving workgroup per row).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream);
 bool decode_uses_w32(int32_t h_q);
