@@ -280,18 +280,23 @@ def cpu_baseline(W, name, budget_s=12.0):
     t0 = time.perf_counter()
     OC.quantize_records(nl64, nr64)                       # the step's append
     t_app = time.perf_counter() - t0
-    done, t_dec, flops = 0, 0.0, 0.0
-    while done < rows and t_dec + t_app < budget_s:
-        recs, local = prepare(done)                       # cache contents: not timed
+    # row decodes until the budget is spent, cycling over the workload's rows
+    # (each row's cache contents are prepared once, untimed)
+    done, t_dec, flops, prepared = 0, 0.0, 0.0, {}
+    while t_dec + t_app < budget_s and done < 64 * rows:
+        r = done % rows
+        if r not in prepared:
+            prepared[r] = prepare(r)
+        recs, local = prepared[r]
         t0 = time.perf_counter()
-        OA.sparse_decode(q[done][None, None], recs, local[None, None], wl.softmax_scale, sink=sink)
+        OA.sparse_decode(q[r][None, None], recs, local[None, None], wl.softmax_scale, sink=sink)
         t_dec += time.perf_counter() - t0
         flops += int((local >= 0).sum()) * FLOP_PER_TOKEN_HEAD * wl.h_q
         done += 1
     cores = len(os.sched_getaffinity(0))
     return dict(value=flops / (t_app + t_dec) / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
-                sample=f"{done} of {rows} query rows of {name} (decode, float64 numpy) plus the "
-                       f"step's {rows}-token quantize-append; {t_app + t_dec:.1f} s",
+                sample=f"{done} query-row decodes of {name} (its {rows} rows cycled; float64 numpy) "
+                       f"plus the step's {rows}-token quantize-append; {t_app + t_dec:.1f} s",
                 seconds=t_app + t_dec)
 
 
@@ -365,7 +370,8 @@ def main():
         "kv_gbps": head["kv_bytes_per_step"] / (head["ms_per_step"] * 1e-3) / 1e9,
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
-                     "kernel": head["kernel"],
+                     "kernel": head["kernel"] + ("+combine_kernel" if head["splits"] > 1 and
+                                                 head["kernel"] == "decode_w32_kernel" else ""),
                      "kernel_us_mean": head["decode_ms_mean"] * 1e3,
                      "other_resource_frac": head["hbm_frac"] if bound == "mfma" else head["mfma_frac"]},
         "cpu_baseline": cpu,
