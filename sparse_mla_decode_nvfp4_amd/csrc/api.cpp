@@ -150,7 +150,8 @@ int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
 }
 
 // Workspace layout for splits > 1 (each region 256-byte aligned):
-//   o_part   [splits, rows, h_q, 512] fp32
+//   o_part   [splits, rows, h_q, 512] fp32 (the 32-head kernel fills the first half
+//            of it with fp16 partials)
 //   lse_part [splits, rows, h_q] fp32
 //   counters [rows, h_q/16] uint32 -- zero on entry, left zero on exit
 struct WsLayout {

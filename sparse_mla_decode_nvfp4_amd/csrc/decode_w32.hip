@@ -31,8 +31,8 @@
 //     2^15 (P stays in fp16 range and rescales of O are rare);
 //   * the four pairs merge their states through LDS at the end (two rounds of
 //     pairwise sums), and each wave writes an eighth of the output dims.
-// Split partials (sink-free O normalised within the split, LSE) are merged by
-// the combine kernel launched right after; all workgroups of a row share an
+// Split partials (sink-free O normalised within the split, in fp16, and LSE)
+// are merged by the combine kernel launched right after; all workgroups of a row share an
 // XCD when the row count allows (the row's records stay in that XCD's L2).
 #include <math.h>
 
@@ -663,9 +663,13 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
                          __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.z, hi.w}, bf16x2))};
         *reinterpret_cast<u32x4*>(a.out + (orow + h) * kVDim + dv0) = v;
       } else {
-        f32x4* d = reinterpret_cast<f32x4*>(a.o_part + (prow + h) * kVDim + dv0);
-        d[0] = lo;
-        d[1] = hi;
+        // split partial in fp16: normalised within the split, so a convex
+        // combination of V rows (|value| <= 6 * 448), rounded to nearest
+        const u32x4 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo.x, lo.y}, f16x2)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo.z, lo.w}, f16x2)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.x, hi.y}, f16x2)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.z, hi.w}, f16x2))};
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o_part) + (prow + h) * kVDim + dv0) = v;
       }
     }
   }
@@ -697,7 +701,8 @@ hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
   // split partials are merged by the combine kernel: the launch boundary
   // makes them visible across XCDs without device-scope fences (on a
   // multi-XCD part those write back and invalidate L2)
-  return launch_combine(a.o_part, a.lse_part, a.splits, a.rows, a.h_q, a.sink, a.out, a.lse, stream);
+  return launch_combine_f16(reinterpret_cast<const uint16_t*>(a.o_part), a.lse_part, a.splits, a.rows,
+                            a.h_q, a.sink, a.out, a.lse, stream);
 }
 
 }  // namespace nvfp4

@@ -49,5 +49,9 @@ bool decode_uses_w32(int32_t h_q);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
                           int64_t rows, int32_t h_q, const float* sink, uint16_t* out,
                           float* lse, hipStream_t stream);
+// The same merge over fp16 partials (the 32-head kernel's own workspace use).
+hipError_t launch_combine_f16(const uint16_t* o_part, const float* lse_part, int32_t splits,
+                              int64_t rows, int32_t h_q, const float* sink, uint16_t* out,
+                              float* lse, hipStream_t stream);
 
 }  // namespace nvfp4
