@@ -1,31 +1,38 @@
-// Sparse MLA decode over 352-byte NVFP4 records, gfx950.
+// Sparse MLA decode over 352-byte NVFP4 records, gfx950: the 16-head kernel
+// (head counts that are not a multiple of 32).
 //
 // What it computes (FlashMLA PR #18 "W4A16 DSA: NVFP4 KV cache format for
 // SM100 sparse decode", PR description): for each query row and head, gather
-// the top-k token records by slot id (negative = invalid), dequantize them to
-// bf16 (NoPE = e2m1 * block scale, RoPE = e4m3), S = scale * Q K^T over the
-// 576 dims with bf16 MFMA and fp32 accumulation, softmax with an optional
-// per-head sink, O = P V over the 512 NoPE dims, also as bf16 MFMA.
+// the top-k token records by slot id (negative = invalid), dequantize them
+// (NoPE = e2m1 * block scale, RoPE = e4m3), S = scale * Q K^T over the 576
+// dims, softmax with an optional per-head sink, O = P V over the 512 NoPE
+// dims, with fp32 accumulation.
 //
-// Kernel organisation ("tile" kernel, 16 heads per workgroup, 4 waves):
+// Kernel organisation (16 heads per workgroup, 4 waves, two workgroups per
+// CU):
 //   * a workgroup owns one query row, one group of 16 heads and one split of
 //     the top-k list, and walks it in 64-token tiles; wave w loads and
 //     dequantizes tokens [16w, 16w+16) of each tile;
 //   * a lane loads the bytes of one token it needs straight from HBM (the
-//     permuted scale layout makes a lane's 8 block scales one 8-byte load),
-//     dequantizes them into the QK MFMA's A operand registers (K never visits
-//     LDS) and writes the NoPE half to the shared V tile;
+//     permuted scale layout makes a lane's 8 block scales one 8-byte load)
+//     and dequantizes them to fp16 QK operands: every E2M1 x E4M3 product has
+//     at most 6 significant bits and lies in [2^-10, 2688], so it is exact in
+//     fp16 (the fp4 convert applies the scale's power of two, one packed
+//     multiply its mantissa); K never visits LDS, the NoPE half goes to the
+//     shared V tile (chunk-major: conflict-free row writes and transposed
+//     reads at immediate offsets);
+//   * Q is converted to fp16 once per wave with a per-head power-of-two scale
+//     folded into the softmax scale (exact for every bf16 element within 2^31
+//     of its head's largest);
 //   * S^T = K Q^T per wave; the per-head tile maximum is exchanged through
-//     LDS so every wave applies the same running max; P (bf16 hi + lo parts)
-//     goes to a shared P tile;
+//     LDS so every wave applies the same running max; P (fp16, relative
+//     error 2^-12) goes to a shared P tile;
 //   * wave w accumulates O[16 heads, dv 128w .. 128w+127] over all 64 tokens
 //     of the tile (V read back with ds_read_b64_tr_b16), so the O accumulator
 //     is 32 registers per lane and two workgroups fit per CU;
 //   * indices are prefetched two tiles ahead and token bytes one tile ahead;
 //   * the running max is only raised (and O rescaled) when a tile exceeds it
-//     by more than 2^8, so rescales are rare;
-//   * P is split into bf16 hi + lo parts (two PV MFMAs): every contraction
-//     stays bf16 while P's rounding error stays far below the tolerance.
+//     by more than 2^8, so rescales are rare.
 // With several splits, the last split of a (row, head group) to finish merges
 // the partial results (LSE-weighted) inside the same launch.
 #include <math.h>
@@ -38,24 +45,26 @@ namespace nvfp4 {
 
 namespace {
 
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_b;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 constexpr int kWaves = 4;
 constexpr int kTile = 16 * kWaves;          // tokens per tile
-constexpr int kVRow = kVDim + 8;            // padded LDS row of the V tile (bf16)
-constexpr int kPRow = kTile + 8;            // padded LDS row of the P tile (bf16)
+// V tile, chunk-major: chunk j (dims 8j .. 8j+7) holds the 64 tokens' 16-byte
+// pieces contiguously, chunks kVChunk bytes apart.  kVChunk = 1088 (64 mod
+// 256): a row write (16 lanes, consecutive tokens, one chunk) covers 256
+// contiguous bytes, and each 32-lane half of a transposed read (tokens
+// {0..3, 8..11} + 4i, two chunks, two 8-byte halves) hits 32 distinct 8-byte
+// bank slots.  Every address is a base register plus an immediate.
+constexpr int kVChunk = kTile * 16 + 64;
+constexpr int kPRow = kTile + 8;            // padded LDS row of the P tile (fp16)
 constexpr float kLazyThreshold = 8.0f;      // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m); }
-
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
-}
-
-// Two fp32 -> packed bf16 (round to nearest even), one instruction.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
 
 // Workgroup barrier ordering LDS accesses only.  __syncthreads() also
 // fences global memory, which makes every wave wait for its outstanding
@@ -72,6 +81,10 @@ __device__ __forceinline__ void lds_barrier() {
 // weights that may flush to zero).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, h16x2));
+}
+
 struct RawTok {          // the bytes one lane needs of one token record
   u32x2 nope[8];         // NoPE blocks 4c+g, c = 0..7
   u32x2 scale;           // scale bytes 8g .. 8g+7 (= blocks 4c+g)
@@ -81,8 +94,8 @@ struct RawTok {          // the bytes one lane needs of one token record
 // Unconditional loads (uniform control flow keeps the prefetch in flight:
 // after a divergent load the compiler can only wait for every outstanding
 // load).  Invalid tokens read record 0, which always exists; their scale
-// bytes are zeroed when consumed (see scale_or_zero), so their NoPE values
-// are exact zeros and cannot carry NaN into P V, and their scores are masked.
+// bytes are zeroed when consumed, so their NoPE values are exact zeros and
+// cannot carry NaN into P V, and their scores are masked.
 __device__ __forceinline__ void load_tok(RawTok& t, const uint8_t* rec, int g) {
 #pragma unroll
   for (int c = 0; c < 8; c++) t.nope[c] = *reinterpret_cast<const u32x2*>(rec + 32 * c + 8 * g);
@@ -103,6 +116,30 @@ __device__ __forceinline__ const uint8_t* rec_ptr(const DecodeArgs& a, int32_t i
   return a.cache + (idx_valid(idx, a.num_slots) ? a.pa.offset((uint32_t)idx) : 0);
 }
 
+// Eight E2M1 codes times a block scale -> eight fp16, exact: the fp4 convert
+// applies the scale's power of two, F (the scale's mantissa as fp16) the rest.
+__device__ __forceinline__ h16x8 dequant8_f16(uint32_t w, float S, h16x2 F) {
+  const h16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 0) * F;
+  const h16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 1) * F;
+  const h16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 2) * F;
+  const h16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 3) * F;
+  return h16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ h16x2 mantissa_f16(float S) {
+  const float Fv = __uint_as_float((__float_as_uint(S) & 0x807FFFFFu) | 0x3F800000u);
+  return __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz(Fv, Fv));   // exact: 4 bits
+}
+
+// Eight E4M3 RoPE bytes -> eight fp16 (exact).
+__device__ __forceinline__ h16x8 rope8_f16(uint32_t x, uint32_t y) {
+  const h16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  const h16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  const h16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y, 1.0f, false);
+  const h16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y, 1.0f, true);
+  return h16x8{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+}
+
 }  // namespace
 
 // Lane l of wave w: g = l/16 (lane group), n = l%16.
@@ -113,18 +150,16 @@ __device__ __forceinline__ const uint8_t* rec_ptr(const DecodeArgs& a, int32_t i
 //   ks 16, 17 cover RoPE dims 16g + 8*(ks-16) + [0,8).  Q is laid out to match.
 //   PV (16x16x32): A = P[head n][token 32ks+8g+i], B = V[token 32ks+8g+i][dv],
 //   C = O[head 4g+r][dv 128w + 16nb + n].
-template <bool kSplitP>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 decode_tile16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[kTile][kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t ptile_hi[16][kPRow];
-  __shared__ __attribute__((aligned(16))) uint16_t ptile_lo[16][kPRow];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * kVChunk];
+  __shared__ __attribute__((aligned(16))) uint16_t ptile[16][kPRow];
   __shared__ float tmax[kWaves][16];
   __shared__ float lsum[kWaves][16];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int n = lane & 15;
 
@@ -145,16 +180,52 @@ decode_tile16_kernel(DecodeArgs a) {
   const int32_t* idx_row = a.indices + (size_t)row * a.topk;
   const int my_tok = 16 * wave + n;                    // this lane's token within a tile
 
-  // ---- Q^T operand registers (head n, k-chunk g)
-  bf16x8 qB[18];
+  // ---- prologue: indices of tiles 0 and 1, token bytes of tile 0 (before
+  // the Q set-up, which hides part of their latency)
+  int tile = tile0;
+  int32_t idx_cur = load_idx(idx_row, tile * kTile + my_tok, t_end);
+  int32_t idx_nxt = load_idx(idx_row, (tile + 1) * kTile + my_tok, t_end);
+  RawTok cur;
+  load_tok(cur, rec_ptr(a, idx_cur), g);
+
+  // ---- Q^T operand registers (head n, k-chunk g) in fp16 with a per-head
+  // power-of-two scale; a negative softmax scale flips Q's sign (exact), so
+  // the score scale is positive
+  h16x8 qB[18];
+  float qscale;          // |softmax_scale| * log2(e) * 2^p of head n
   {
     const uint16_t* qrow = a.q + ((size_t)row * a.h_q + h0 + n) * kQkDim;
+    u32x4 raw[18];
 #pragma unroll
     for (int ks = 0; ks < 16; ks++)
-      qB[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * (4 * (ks >> 1) + g) + 8 * (ks & 1));
+      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * (4 * (ks >> 1) + g) + 8 * (ks & 1));
 #pragma unroll
     for (int ks = 16; ks < 18; ks++)
-      qB[ks] = *reinterpret_cast<const bf16x8*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
+      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
+    uint32_t am = 0;
+#pragma unroll
+    for (int ks = 0; ks < 18; ks++)
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const uint32_t x = raw[ks][w];
+        am = max(am, max((x << 16) & 0x7FFFFFFFu, x & 0x7FFF0000u));
+      }
+    am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    // largest magnitude's exponent e: scale by 2^-(e-14) so it lands in [2^14, 2^15)
+    int e = (int)(am >> 23) - 127;
+    if (am == 0 || am >= 0x7F800000u) e = 14;
+    const int p = max(e - 14, -100);
+    const float mul = a.scale_log2 < 0.f ? -__builtin_ldexpf(1.0f, -p) : __builtin_ldexpf(1.0f, -p);
+    qscale = fabsf(a.scale_log2) * __builtin_ldexpf(1.0f, p);
+#pragma unroll
+    for (int ks = 0; ks < 18; ks++)
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const uint32_t x = raw[ks][w];
+        qB[ks][2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
+        qB[ks][2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+      }
   }
 
   f32x4 acc_o[8];
@@ -166,14 +237,13 @@ decode_tile16_kernel(DecodeArgs a) {
   float m_r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float l_part = 0.f;          // this lane's share of head n's denominator
 
-  // ---- prologue: indices of tiles 0 and 1, token bytes of tile 0
-  int tile = tile0;
-  int32_t idx_cur = load_idx(idx_row, tile * kTile + my_tok, t_end);
-  int32_t idx_nxt = load_idx(idx_row, (tile + 1) * kTile + my_tok, t_end);
-  RawTok cur;
-  load_tok(cur, rec_ptr(a, idx_cur), g);
+  // V tile addresses.  Write (k-step 2c+h): chunk 8c + 2g + h, token
+  // my_tok.  Read (PV k-step ks, half hb, block nb): token 32ks + 8g + 4hb +
+  // (l%16)/4, chunk 16w + 2nb + ((l%4)>>1), byte 8(l&1).
+  const uint32_t vw_base = (uint32_t)(size_t)(vtile + 2 * g * kVChunk + my_tok * 16);
+  const uint32_t vr_base = (uint32_t)(size_t)(vtile + (16 * wave + ((lane & 3) >> 1)) * kVChunk +
+                                             (8 * g + ((lane >> 2) & 3)) * 16 + 8 * (lane & 1));
 
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   // One tile step.  `cur` holds this lane's bytes of tile t, `nxt` receives
   // tile t+1's; the loop below alternates the two buffers so the prefetched
   // bytes are never copied.
@@ -181,10 +251,17 @@ decode_tile16_kernel(DecodeArgs a) {
     // ---- prefetch: indices two tiles ahead, token bytes one tile ahead
     const int32_t idx_nn = load_idx(idx_row, (t + 2) * kTile + my_tok, t_end);
     load_tok(nxt, rec_ptr(a, idx_nxt), g);
+    // keep the prefetch at the top of the step: the scheduler would otherwise
+    // sink these loads below the dequant and shorten their lead time
+    __builtin_amdgcn_sched_barrier(0);
     const bool cur_valid = idx_valid(idx_cur, a.num_slots);
     const uint64_t vmask = __ballot(cur_valid);
 
-    // ---- dequantize this wave's 16 tokens into K operand registers
+    // all waves are done reading the previous tile's V and P
+    lds_barrier();
+    // ---- dequantize this wave's 16 tokens k-step by k-step: each K operand
+    // goes to the V tile (NoPE) and straight into S^T = K Q^T (two
+    // accumulation chains)
     const uint32_t scx = cur_valid ? cur.scale.x : 0u;
     const uint32_t scy = cur_valid ? cur.scale.y : 0u;
     const f32x2 s01 = e4m3x2_to_f32<0>(scx);
@@ -192,36 +269,25 @@ decode_tile16_kernel(DecodeArgs a) {
     const f32x2 s45 = e4m3x2_to_f32<0>(scy);
     const f32x2 s67 = e4m3x2_to_f32<1>(scy);
     const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
-    u32x4 kA[18];
+    f32x4 s_acc = {0.f, 0.f, 0.f, 0.f}, s_acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; c++) {
-      uint32_t o[4];
-      dequant8(cur.nope[c].x, sc[c], o);
-      kA[2 * c] = u32x4{o[0], o[1], o[2], o[3]};
-      dequant8(cur.nope[c].y, sc[c], o);
-      kA[2 * c + 1] = u32x4{o[0], o[1], o[2], o[3]};
+      const h16x2 F = mantissa_f16(sc[c]);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const h16x8 k = dequant8_f16(h ? cur.nope[c].y : cur.nope[c].x, sc[c], F);
+        *reinterpret_cast<__attribute__((address_space(3))) h16x8*>(
+            (lds_b*)(size_t)vw_base + (8 * c + h) * kVChunk) = k;
+        if (h == 0) s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c], s_acc, 0, 0, 0);
+        else s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c + 1], s_acc1, 0, 0, 0);
+      }
     }
-    kA[16] = u32x4{e4m3x2_to_bf16x2<0>(cur.rope.x), e4m3x2_to_bf16x2<1>(cur.rope.x),
-                   e4m3x2_to_bf16x2<0>(cur.rope.y), e4m3x2_to_bf16x2<1>(cur.rope.y)};
-    kA[17] = u32x4{e4m3x2_to_bf16x2<0>(cur.rope.z), e4m3x2_to_bf16x2<1>(cur.rope.z),
-                   e4m3x2_to_bf16x2<0>(cur.rope.w), e4m3x2_to_bf16x2<1>(cur.rope.w)};
-
-    // all waves are done reading the previous tile's V and P
-    lds_barrier();
-#pragma unroll
-    for (int ks = 0; ks < 16; ks++)
-      *reinterpret_cast<u32x4*>(&vtile[my_tok][16 * (4 * (ks >> 1) + g) + 8 * (ks & 1)]) = kA[ks];
-
-    // ---- S^T = K Q^T for this wave's tokens
-    f32x4 s_acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 18; ks++)
-      s_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kA[ks]), qB[ks],
-                                                      s_acc, 0, 0, 0);
+    s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rope8_f16(cur.rope.x, cur.rope.y), qB[16], s_acc, 0, 0, 0);
+    s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(rope8_f16(cur.rope.z, cur.rope.w), qB[17], s_acc1, 0, 0, 0);
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; r++)
-      s[r] = ((vmask >> (4 * g + r)) & 1ull) ? s_acc[r] * a.scale_log2 : -INFINITY;
+      s[r] = ((vmask >> (4 * g + r)) & 1ull) ? (s_acc[r] + s_acc1[r]) * qscale : -INFINITY;
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     bm = fmaxf(bm, shfl_xor(bm, 16));
     bm = fmaxf(bm, shfl_xor(bm, 32));
@@ -257,44 +323,26 @@ decode_tile16_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; r++) acc_o[nb][r] *= alpha[r];
     }
 
-    // ---- P for this wave's tokens -> P tile (bf16 hi and lo parts)
+    // ---- P for this wave's tokens -> P tile (fp16)
     const float m_safe = (m_n == -INFINITY) ? 0.f : m_n;   // s = -inf -> p = 0
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) p[r] = fast_exp2(s[r] - m_safe);
     l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    {
-      const uint32_t hi01 = pack_bf16x2(p[0], p[1]);
-      const uint32_t hi23 = pack_bf16x2(p[2], p[3]);
-      const int col = 16 * wave + 4 * g;
-      *reinterpret_cast<u32x2*>(&ptile_hi[n][col]) = u32x2{hi01, hi23};
-      if (kSplitP) {
-        const uint32_t lo01 = pack_bf16x2(p[0] - __uint_as_float(hi01 << 16),
-                                          p[1] - __uint_as_float(hi01 & 0xFFFF0000u));
-        const uint32_t lo23 = pack_bf16x2(p[2] - __uint_as_float(hi23 << 16),
-                                          p[3] - __uint_as_float(hi23 & 0xFFFF0000u));
-        *reinterpret_cast<u32x2*>(&ptile_lo[n][col]) = u32x2{lo01, lo23};
-      }
-    }
+    *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) = u32x2{pack_h16x2(p[0], p[1]), pack_h16x2(p[2], p[3])};
     lds_barrier();                        // P and V tiles complete
 
     // ---- O[:, 128w .. 128w+127] += P V over the tile's 64 tokens
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-      const int t8 = 32 * ks + 8 * g;
-      const bf16x8 pa_hi = *reinterpret_cast<const bf16x8*>(&ptile_hi[n][t8]);
-      bf16x8 pa_lo;
-      if (kSplitP) pa_lo = *reinterpret_cast<const bf16x8*>(&ptile_lo[n][t8]);
-      const uint16_t* vb0 = &vtile[t8 + (n >> 2)][128 * wave + 4 * (n & 3)];
-      const uint16_t* vb1 = vb0 + 4 * kVRow;
+      const h16x8 pa = *reinterpret_cast<const h16x8*>(&ptile[n][32 * ks + 8 * g]);
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
-        const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb0 + 16 * nb));
-        const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb1 + 16 * nb));
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, bv, acc_o[nb], 0, 0, 0);
-        if (kSplitP)
-          acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, bv, acc_o[nb], 0, 0, 0);
+        lds_b* const rb = (lds_b*)(size_t)vr_base + 2 * nb * kVChunk + 32 * ks * 16;
+        const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)rb);
+        const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(rb + 4 * 16));
+        const h16x8 bv = __builtin_bit_cast(h16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc_o[nb], 0, 0, 0);
       }
     }
     idx_cur = idx_nxt;
@@ -336,7 +384,7 @@ decode_tile16_kernel(DecodeArgs a) {
       const int h = 4 * g + r;
       const float v = acc_o[nb][r] * inv[r];
       if (a.splits == 1)
-        a.out[(orow + h) * kVDim + dv] = (uint16_t)bf16_rne(v);
+        a.out[(orow + h) * kVDim + dv] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)v);
       else
         a.o_part[(prow + h) * kVDim + dv] = v;
     }
@@ -381,7 +429,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   if (decode_uses_w32(a.h_q)) return launch_decode_w32(a, stream);
   const int grid = a.rows * (a.h_q / 16) * a.splits;
-  hipLaunchKernelGGL((decode_tile16_kernel<true>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL(decode_tile16_kernel, dim3(grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
