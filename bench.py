@@ -119,6 +119,12 @@ def fill_pool(lib, W, wl, dev):
     return cache
 
 
+def decode_kernel_name(h_q):
+    """The decode kernel the library picks for h_q heads (32- or 16-head
+    workgroups)."""
+    return "decode_w32_kernel" if h_q % 32 == 0 else "decode_tile16_kernel"
+
+
 def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_splits=0):
     import torch
     t_gen = time.time()
@@ -200,7 +206,7 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     dec_avg = float(dec_ms.mean())
     res = dict(
         workload=name, description=wl.description, rows=rows, h_q=wl.h_q, topk=wl.topk,
-        kernel="decode_w32_kernel" if wl.h_q % 32 == 0 else "decode_tile16_kernel",
+        kernel=decode_kernel_name(wl.h_q),
         splits=splits, sets=nsets, ms_per_step=step_ms,
         decode_ms_mean=dec_avg, decode_ms_median=float(np.median(dec_ms)),
         decode_ms_min=float(dec_ms.min()),
@@ -361,7 +367,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16" if head["kernel"] == "decode_w32_kernel" else "bf16",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": 32, "s_q": 1, "h_q": 64, "topk": 2048,
                    "d_qk": 576, "d_v": 512, "record_bytes": 352, "block_size": 64,
@@ -371,7 +377,7 @@ def main():
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "kernel": head["kernel"] + ("+combine_kernel" if head["splits"] > 1 and
-                                                 head["kernel"] == "decode_w32_kernel" else ""),
+                                                 head["kernel"] != "decode_tile16_kernel" else ""),
                      "kernel_us_mean": head["decode_ms_mean"] * 1e3,
                      "other_resource_frac": head["hbm_frac"] if bound == "mfma" else head["mfma_frac"]},
         "cpu_baseline": cpu,
