@@ -231,11 +231,16 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     return res
 
 
-def bench_append(lib, W, steps, warmup, dev):
+def bench_append(lib, W, steps, warmup, dev, fp16=False):
+    """The append_write workload through the bf16 export, or with the same
+    latents cast to fp16 through the fp16 export."""
     import torch
     wl = W.append_write()
+    name = "append_write_fp16" if fp16 else "append_write"
     cache = torch.from_numpy(wl.sentinel.reshape(wl.num_blocks, wl.block_size, 352)).to(dev)
     lat, rope = wl.latent.to(dev), wl.rope.to(dev)
+    if fp16:
+        lat, rope = lat.to(torch.float16), rope.to(torch.float16)
     sm = torch.from_numpy(wl.slot_mapping).to(dev)
     for _ in range(warmup):
         lib.quantize_append(lat, rope, sm, cache)
@@ -250,11 +255,11 @@ def bench_append(lib, W, steps, warmup, dev):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     mapped = int((wl.slot_mapping >= 0).sum())
     nbytes = mapped * (512 * 2 + 64 * 2 + 352) + wl.num_tokens * 8
-    res = dict(workload="append_write", tokens=wl.num_tokens, mapped=mapped, ms=ms,
+    res = dict(workload=name, tokens=wl.num_tokens, mapped=mapped, ms=ms,
                bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9,
                tokens_per_s=mapped / (ms * 1e-3))
     res["hbm_frac"] = res["gbps"] / PEAK_HBM_GBS
-    log(f"append_write: {ms * 1e3:.1f} us, {res['gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM)")
+    log(f"{name}: {ms * 1e3:.1f} us, {res['gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM)")
     del cache
     torch.cuda.empty_cache()
     return res
@@ -332,8 +337,8 @@ def main():
     use_graph = args.graph
 
     if args.only:
-        if args.only == "append_write":
-            res = bench_append(lib, W, args.steps, args.warmup, dev)
+        if args.only in ("append_write", "append_write_fp16"):
+            res = bench_append(lib, W, args.steps, args.warmup, dev, fp16=args.only.endswith("fp16"))
         else:
             res = bench_decode(lib, W, args.only, args.steps, args.warmup, args.sets, use_graph, dev,
                                args.splits)
@@ -349,6 +354,8 @@ def main():
                                            max(5, args.warmup // 2), args.sets, use_graph, dev)
         extra["append_write"] = bench_append(lib, W, max(20, args.steps // 2),
                                              max(5, args.warmup // 2), dev)
+        extra["append_write_fp16"] = bench_append(lib, W, max(20, args.steps // 2),
+                                                  max(5, args.warmup // 2), dev, fp16=True)
     cpu = None if args.no_cpu else cpu_baseline(W, args.workload)
 
     bound = head["bound"]

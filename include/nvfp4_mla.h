@@ -112,6 +112,22 @@ int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride
                               void* stream);
 
 /*
+ * Quantize-append from fp16 inputs: the same write rule and 352-byte record
+ * as nvfp4_mla_quantize_append, with latent and RoPE given as IEEE fp16
+ * instead of bf16 (the write kernel of vLLM PR #82 is dispatched over both
+ * 16-bit float types: the review thread on its host launch).  Every fp16
+ * value is exact in fp32, so the scale, code and RoPE rounding is the one
+ * stated above, applied to the fp16 values.  Arguments, layouts, alignment,
+ * ownership, skipping and errors are those of nvfp4_mla_quantize_append.
+ */
+int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_stride,
+                                   const void* rope_fp16, int64_t rope_row_stride,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   uint8_t* kv_cache, int64_t num_blocks,
+                                   int32_t block_size, int64_t block_stride_bytes,
+                                   void* stream);
+
+/*
  * Dequantize-gather: out[i, :] = the 576 bf16 values of the record at
  * slots[i] ([512 NoPE = e2m1 * scale | 64 RoPE]), exactly as the decode
  * dequantizes them (every value is exact in bf16).  slots[i] < 0 or beyond

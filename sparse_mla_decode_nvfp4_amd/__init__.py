@@ -40,6 +40,8 @@ SIGNATURES = {
     "nvfp4_mla_check_format": (ctypes.c_int, [_I32, _I32, _I32, _I32]),
     "nvfp4_mla_quantize_append": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I32,
                                                  _I64, _P]),
+    "nvfp4_mla_quantize_append_fp16": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                                      _I32, _I64, _P]),
     "nvfp4_mla_dequantize_gather": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _I64, _P, _P]),
     "nvfp4_mla_sparse_decode_plan": (ctypes.c_int, [_I32, _I32, _I32, _I32,
                                                     ctypes.POINTER(ctypes.c_int32)]),
@@ -123,21 +125,23 @@ def new_cache(num_blocks, block_size, device="cuda", fill=0):
 def quantize_append(latent, rope, slot_mapping, kv_cache):
     """Writes NVFP4 records for each token with slot_mapping >= 0, in place.
 
-    latent: bf16 [N, >=512] (rows 16-byte aligned), rope: bf16 [N, >=64],
-    slot_mapping: int64 [N], kv_cache: uint8 [num_blocks, block_size, 352].
+    latent: bf16 or fp16 [N, >=512] (rows 16-byte aligned), rope: the same
+    dtype [N, >=64], slot_mapping: int64 [N], kv_cache: uint8 [num_blocks,
+    block_size, 352].
     """
     n = latent.shape[0]
-    if latent.dtype != torch.bfloat16 or rope.dtype != torch.bfloat16:
-        raise ValueError("latent and rope must be bfloat16")
+    if latent.dtype not in (torch.bfloat16, torch.float16) or rope.dtype != latent.dtype:
+        raise ValueError("latent and rope must both be bfloat16 or both float16")
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n or rope.shape[0] != n:
         raise ValueError("slot_mapping must be int64 [N] matching latent/rope rows")
     if latent.stride(-1) != 1 or rope.stride(-1) != 1 or not slot_mapping.is_contiguous():
         raise ValueError("inner dimensions must be contiguous")
     nb, bs, stride = _cache_geometry(kv_cache)
-    code = lib().nvfp4_mla_quantize_append(
+    fn = "nvfp4_mla_quantize_append" + ("_fp16" if latent.dtype == torch.float16 else "")
+    code = getattr(lib(), fn)(
         _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(slot_mapping), n,
         _ptr(kv_cache), nb, bs, stride, _stream(kv_cache.device))
-    _check("nvfp4_mla_quantize_append", code)
+    _check(fn, code)
     return kv_cache
 
 

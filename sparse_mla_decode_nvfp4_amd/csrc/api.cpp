@@ -179,28 +179,14 @@ size_t workspace_bytes(int64_t rows, int32_t h_q, int32_t splits) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int nvfp4_mla_abi_version(void) { return NVFP4_MLA_ABI_VERSION; }
-
-const char* nvfp4_mla_last_error(void) { return g_last_error.c_str(); }
-
-int nvfp4_mla_check_format(int32_t record_bytes, int32_t nope_dim, int32_t rope_dim,
-                           int32_t v_dim) {
-  if (record_bytes != NVFP4_MLA_RECORD_BYTES || nope_dim != NVFP4_MLA_NOPE_DIM ||
-      rope_dim != NVFP4_MLA_ROPE_DIM || v_dim != NVFP4_MLA_V_DIM)
-    return fail(NVFP4_MLA_ERR_UNSUPPORTED_FORMAT,
-                "unsupported format: record %d B, NoPE %d, RoPE %d, d_v %d (this library "
-                "implements the 352 B NVFP4 record with 512/64/512)",
-                record_bytes, nope_dim, rope_dim, v_dim);
-  return ok();
-}
-
-int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride,
-                              const void* rope_bf16, int64_t rope_row_stride,
-                              const int64_t* slot_mapping, int64_t num_tokens,
-                              uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                              int64_t block_stride_bytes, void* stream) {
+// Shared by the bf16 and fp16 exports: the same checks, one kernel template.
+int quantize_append_impl(const char* fn, const void* latent_bf16, int64_t latent_row_stride,
+                         const void* rope_bf16, int64_t rope_row_stride,
+                         const int64_t* slot_mapping, int64_t num_tokens, uint8_t* kv_cache,
+                         int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                         bool f16_input, void* stream) {
   if (num_tokens < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
   int64_t num_slots = 0;
   int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
@@ -225,11 +211,51 @@ int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride
   hipError_t e = nvfp4::launch_quantize_append(
       static_cast<const uint16_t*>(latent_bf16), latent_row_stride,
       static_cast<const uint16_t*>(rope_bf16), rope_row_stride, slot_mapping, num_tokens, kv_cache,
-      num_slots, make_page_addr(block_size, block_stride_bytes),
+      num_slots, make_page_addr(block_size, block_stride_bytes), f16_input,
       static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
-    return fail(NVFP4_MLA_ERR_HIP, "quantize_append launch failed: %s", hipGetErrorString(e));
+    return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_mla_abi_version(void) { return NVFP4_MLA_ABI_VERSION; }
+
+const char* nvfp4_mla_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_mla_check_format(int32_t record_bytes, int32_t nope_dim, int32_t rope_dim,
+                           int32_t v_dim) {
+  if (record_bytes != NVFP4_MLA_RECORD_BYTES || nope_dim != NVFP4_MLA_NOPE_DIM ||
+      rope_dim != NVFP4_MLA_ROPE_DIM || v_dim != NVFP4_MLA_V_DIM)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_FORMAT,
+                "unsupported format: record %d B, NoPE %d, RoPE %d, d_v %d (this library "
+                "implements the 352 B NVFP4 record with 512/64/512)",
+                record_bytes, nope_dim, rope_dim, v_dim);
+  return ok();
+}
+
+
+int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride,
+                              const void* rope_bf16, int64_t rope_row_stride,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                              int64_t block_stride_bytes, void* stream) {
+  return quantize_append_impl("quantize_append", latent_bf16, latent_row_stride, rope_bf16,
+                              rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
+                              block_size, block_stride_bytes, false, stream);
+}
+
+int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_stride,
+                                   const void* rope_fp16, int64_t rope_row_stride,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                                   int64_t block_stride_bytes, void* stream) {
+  return quantize_append_impl("quantize_append_fp16", latent_fp16, latent_row_stride, rope_fp16,
+                              rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
+                              block_size, block_stride_bytes, true, stream);
 }
 
 int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,

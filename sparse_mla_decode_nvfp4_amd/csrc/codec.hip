@@ -34,9 +34,19 @@ __device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
   return s == 0.0f ? 0u : c;
 }
 
+// A 16-bit input element (bf16, or fp16 when kF16) widened to fp32, exactly.
+template <bool kF16>
+__device__ __forceinline__ float widen16(uint32_t bits16) {
+  if constexpr (kF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  else return __uint_as_float(bits16 << 16);
+}
+
 // One wavefront per token; 4 tokens per 256-thread block.  Lane l quantizes
 // NoPE elements [8l, 8l+8) (block l/2) and RoPE element l; the record is
-// assembled in LDS and written with 22 16-byte stores.
+// assembled in LDS and written with 22 16-byte stores.  The input is bf16, or
+// fp16 when kF16: every fp16 or bf16 value is exact in fp32, so the rounding
+// below is the same for both.
+template <bool kF16>
 __global__ void __launch_bounds__(256)
 quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
                        const uint16_t* __restrict__ rope, int64_t rstride,
@@ -56,8 +66,8 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    x[2 * i] = __uint_as_float(raw[i] << 16);
-    x[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+    x[2 * i] = widen16<kF16>(raw[i] & 0xFFFFu);
+    x[2 * i + 1] = widen16<kF16>(raw[i] >> 16);
   }
   float amax = 0.0f;
 #pragma unroll
@@ -74,7 +84,7 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
   reinterpret_cast<uint32_t*>(r)[lane] = packed;
   if ((lane & 1) == 0) r[kScaleOffset + scale_byte(lane >> 1)] = (uint8_t)scode;
   // ---- RoPE: lane l handles element l
-  const float rv = __uint_as_float((uint32_t)rope[tok * rstride + lane] << 16);
+  const float rv = widen16<kF16>((uint32_t)rope[tok * rstride + lane]);
   const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
   r[kRopeOffset + lane] = (uint8_t)rcode;
   __builtin_amdgcn_wave_barrier();
@@ -123,12 +133,17 @@ hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
                                   const uint16_t* rope, int64_t rstride,
                                   const int64_t* slot_mapping, int64_t num_tokens,
                                   uint8_t* cache, int64_t num_slots, const PageAddr& pa,
-                                  hipStream_t stream) {
+                                  bool f16_input, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int64_t blocks = (num_tokens + 3) / 4;
-  hipLaunchKernelGGL(quantize_append_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
-                     num_slots, pa);
+  if (f16_input)
+    hipLaunchKernelGGL(quantize_append_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
+                       num_slots, pa);
+  else
+    hipLaunchKernelGGL(quantize_append_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
+                       num_slots, pa);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
                                   const uint16_t* rope, int64_t rstride,
                                   const int64_t* slot_mapping, int64_t num_tokens,
                                   uint8_t* cache, int64_t num_slots, const PageAddr& pa,
-                                  hipStream_t stream);
+                                  bool f16_input, hipStream_t stream);
 
 hipError_t launch_dequantize_gather(const uint8_t* cache, int64_t num_slots, const PageAddr& pa,
                                     const int32_t* slots, int64_t n, uint16_t* out,

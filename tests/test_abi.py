@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = m.lib()
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for name in names:
         assert hasattr(lib, name), name
         assert name in m.SIGNATURES, name
@@ -50,13 +50,13 @@ def test_check_format_accepts_only_the_352_byte_record():
         assert "unsupported format" in m.last_error()
 
 
-def qa(**kw):
+def qa(fn="nvfp4_mla_quantize_append", **kw):
     a = dict(latent=P16, lstride=512, rope=P16, rstride=64, slots=P16, n=4, cache=P16,
              nblocks=4, bs=64, stride=64 * 352, stream=NULL)
     a.update(kw)
-    return m.lib().nvfp4_mla_quantize_append(a["latent"], a["lstride"], a["rope"], a["rstride"],
-                                             a["slots"], a["n"], a["cache"], a["nblocks"],
-                                             a["bs"], a["stride"], a["stream"])
+    return getattr(m.lib(), fn)(a["latent"], a["lstride"], a["rope"], a["rstride"],
+                                a["slots"], a["n"], a["cache"], a["nblocks"],
+                                a["bs"], a["stride"], a["stream"])
 
 
 @pytest.mark.parametrize("kw, needle", [
@@ -75,8 +75,9 @@ def qa(**kw):
     (dict(lstride=520 + 4), "16-byte aligned"),
     (dict(latent=ctypes.c_void_p(0x100004)), "16-byte aligned"),
 ])
-def test_quantize_append_rejects_bad_arguments(kw, needle):
-    assert qa(**kw) == m.ERR_INVALID_ARGUMENT
+@pytest.mark.parametrize("fn", ["nvfp4_mla_quantize_append", "nvfp4_mla_quantize_append_fp16"])
+def test_quantize_append_rejects_bad_arguments(fn, kw, needle):
+    assert qa(fn, **kw) == m.ERR_INVALID_ARGUMENT
     assert needle in m.last_error()
 
 

@@ -25,6 +25,7 @@ def bf16_from_f64(x):
 
 
 def gpu_quantize(lib, latent_bf16, rope_bf16, num_slots=None, bs=64, sentinel=None):
+    """Quantize-append of bf16 (or fp16) rows to slots 0..N-1 on the GPU."""
     n = latent_bf16.shape[0]
     if num_slots is None:
         num_slots = ((n + bs - 1) // bs) * bs
@@ -213,3 +214,91 @@ def test_zero_tokens_is_a_no_op(lib):
                         torch.zeros((0,), dtype=torch.int64, device=DEV), cache)
     torch.cuda.synchronize()
     assert bool((cache == 7).all())
+
+
+# ---- fp16 input (the write kernel's other 16-bit input type)
+
+def fp16_from_f64(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(torch.float16)
+
+
+def test_fp16_every_amax_gives_the_oracle_scale(lib):
+    """All positive finite fp16 values as a block amax, through the fp16
+    export, with companions below it in the block."""
+    bits = torch.arange(1, 0x7C00, dtype=torch.int32).to(torch.int16)
+    amax = bits.view(torch.float16).to(torch.float64).numpy()
+    n = len(amax)
+    lat = np.zeros((n, 512))
+    lat[:, 3] = amax
+    lat[:, 4] = -amax * 0.3
+    lat[:, 7] = amax * 0.74
+    lat[:, 16:32] = -np.linspace(0, 1, 16)[None, :] * amax[:, None]
+    lat_h = fp16_from_f64(lat)
+    rope_h = fp16_from_f64(np.zeros((n, 64)))
+    got = gpu_quantize(lib, lat_h, rope_h)
+    ref = OC.quantize_records(f64(lat_h), f64(rope_h))
+    assert np.array_equal(got, ref), f"{int(np.any(got != ref, axis=1).sum())} records differ"
+
+
+def test_fp16_every_code_under_every_scale(lib):
+    """For each E4M3 scale code S (amax = 6*value(S), exact in fp16 where it
+    fits), every fp16 x with |x| <= amax in the other lanes of the block."""
+    pos = torch.arange(0, 0x7C00, dtype=torch.int32).to(torch.int16).view(torch.float16)
+    pos = pos.to(torch.float64).numpy()
+    rows = []
+    for s in range(1, 0x7F):
+        amax = 6.0 * OF.e4m3_decode(s)
+        xs = pos[pos <= amax]
+        xs = np.concatenate([xs, -xs])
+        per = 15
+        ng = (len(xs) + per - 1) // per
+        blk = np.zeros((ng, 16))
+        flat = np.zeros(ng * per)
+        flat[:len(xs)] = xs
+        blk[:, :15] = flat.reshape(ng, per)
+        blk[:, 15] = amax
+        rows.append(blk)
+    blocks = np.concatenate(rows)
+    nt = (len(blocks) + 31) // 32
+    pad = np.zeros((nt * 32 - len(blocks), 16))
+    lat = np.concatenate([blocks, pad]).reshape(nt, 512)
+    note(f"fp16 code sweep: {len(blocks)} blocks in {nt} tokens")
+    lat_h = fp16_from_f64(lat)
+    rope_h = fp16_from_f64(np.zeros((nt, 64)))
+    got = gpu_quantize(lib, lat_h, rope_h)
+    ref = OC.quantize_records(f64(lat_h), f64(rope_h))
+    bad = np.any(got != ref, axis=1)
+    assert not bad.any(), f"{int(bad.sum())} records differ, first token {np.nonzero(bad)[0][:3]}"
+
+
+def test_fp16_every_finite_value_as_rope(lib):
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    v = bits.view(torch.float16)
+    v = v[torch.isfinite(v.to(torch.float32))]
+    n = (len(v) + 63) // 64
+    rope = torch.zeros(n * 64, dtype=torch.float16)
+    rope[:len(v)] = v
+    rope = rope.reshape(n, 64)
+    lat_h = torch.zeros((n, 512), dtype=torch.float16)
+    got = gpu_quantize(lib, lat_h, rope)
+    ref = OC.quantize_records(f64(lat_h), f64(rope))
+    assert np.array_equal(got, ref)
+
+
+def test_fp16_workload_over_sentinel_bytes(lib):
+    """Seeded fp16 latents (the append workload's recipe, cast to fp16, plus
+    values beyond bf16 precision and near the fp16 range) scattered into a
+    sentinel cache through a slot map with -1 entries."""
+    wl = W.append_write(num_tokens=2048, num_slots=8192)
+    g = np.random.default_rng([3, 9, 0])
+    lat = wl.latent.to(torch.float64).numpy() * (1 + g.uniform(-1e-3, 1e-3, size=(2048, 512)))
+    lat[::97] = np.clip(lat[::97] * 3000.0, -65000.0, 65000.0)   # rows near the fp16 range top
+    rope = wl.rope.to(torch.float64).numpy()
+    lat_h, rope_h = fp16_from_f64(lat), fp16_from_f64(rope)
+    cache = torch.from_numpy(wl.sentinel.reshape(wl.num_blocks, wl.block_size, 352)).to(DEV)
+    lib.quantize_append(lat_h.to(DEV), rope_h.to(DEV), torch.from_numpy(wl.slot_mapping).to(DEV), cache)
+    torch.cuda.synchronize()
+    got = cache.view(-1, 352).cpu().numpy()
+    ref = OC.quantize_append(wl.sentinel, f64(lat_h), f64(rope_h), wl.slot_mapping)
+    diff = np.nonzero(np.any(got != ref, axis=1))[0]
+    assert diff.size == 0, f"{diff.size} slots differ, first {diff[:5]}"

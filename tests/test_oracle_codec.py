@@ -41,6 +41,23 @@ def test_block_scale_is_e4m3_of_amax_over_6_for_every_bf16_amax():
     assert np.all(C.block_scales(np.zeros((1, 512))) == 0)
 
 
+def test_block_scale_is_e4m3_of_amax_over_6_for_every_fp16_amax():
+    """The fp16-input write path uses the same rule: for every positive
+    finite fp16 amax the oracle's exact-quotient scale equals torch's
+    float8_e4m3fn rounding of the correctly rounded fp32 quotient (so fp32
+    division is exact enough for fp16 inputs too)."""
+    bits = torch.arange(1, 0x7C00, dtype=torch.int32).to(torch.int16)
+    amax = bits.view(torch.float16).to(torch.float64).numpy()
+    lat = np.zeros((len(amax), 512))
+    lat[:, 9] = -amax
+    got = C.block_scales(lat)[:, 0]
+    q = torch.from_numpy(amax).to(torch.float32) / 6.0
+    inrange = (q < 464.0).numpy()
+    ref = q[inrange].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got[inrange], ref)
+    assert np.all(got[~inrange] == 0x7E)
+
+
 def crafted_token():
     """Block s: elements i = 0..14 are sign(i) * grid[i % 8] * v_s with the
     sign negative for i >= 8, element 15 is 6 * v_s (the amax), where v_s is
