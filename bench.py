@@ -86,16 +86,26 @@ def measured_traffic(workload):
 
 
 # --------------------------------------------------------------------------- decode
+def index_lists(s):
+    """(index array, slot count of its cache) of each list of a decode step:
+    one for the plain decode, primary and extra for the dual-cache decode."""
+    if hasattr(s, "extra_indices"):
+        return [(s.indices, s.primary.num_slots), (s.extra_indices, s.extra_pool.num_slots)]
+    return [(s.indices, s.num_slots)]
+
+
 def decode_accounting(sets, wl):
     """Algorithmic flops and bytes per step (averaged over the sets)."""
     fl, kv, uniq = [], [], []
     for s in sets:
-        idx = s.indices
-        valid = (idx >= 0) & (idx < wl.num_slots)
-        nv = int(valid.sum())
+        nv = nu = 0
+        for idx, n_slots in index_lists(s):
+            valid = (idx >= 0) & (idx < n_slots)
+            nv += int(valid.sum())
+            nu += len(np.unique(idx[valid]))
         fl.append(nv * FLOP_PER_TOKEN_HEAD * wl.h_q)
         kv.append(nv * 352)
-        uniq.append(len(np.unique(idx[valid])) * 352)
+        uniq.append(nu * 352)
     rows = wl.batch * wl.s_q
     other = (rows * wl.h_q * 576 * 2 + rows * wl.h_q * 512 * 2 + rows * wl.h_q * 4
              + rows * wl.topk * 4 + wl.h_q * 4)
@@ -103,15 +113,18 @@ def decode_accounting(sets, wl):
                 unique_bytes=float(np.mean(uniq)) + other, other_bytes=other)
 
 
-def fill_pool(lib, W, wl, dev):
+def fill_pool(lib, W, config_id, num_blocks, block_size, seed, dev):
+    """A paged cache with every slot holding a record quantized (by the HIP
+    append) from seeded random latents of the workload's distribution."""
     import torch
-    cache = lib.new_cache(wl.num_blocks, wl.block_size, dev)
+    cache = lib.new_cache(num_blocks, block_size, dev)
     gen = torch.Generator(device=dev)
-    gen.manual_seed(1000 + wl.config_id)
+    gen.manual_seed(seed)
     chunk = 1 << 20
-    for start in range(0, wl.num_slots, chunk):
-        n = min(chunk, wl.num_slots - start)
-        lat, rope = W.latents_torch(wl.config_id, n, gen, dev)
+    num_slots = num_blocks * block_size
+    for start in range(0, num_slots, chunk):
+        n = min(chunk, num_slots - start)
+        lat, rope = W.latents_torch(config_id, n, gen, dev)
         sm = torch.arange(start, start + n, dtype=torch.int64, device=dev)
         lib.quantize_append(lat, rope, sm, cache)
         del lat, rope, sm
@@ -128,11 +141,17 @@ def decode_kernel_name(h_q):
 def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_splits=0):
     import torch
     t_gen = time.time()
-    sets = [W.DECODE_WORKLOADS[name](rep=r, with_latents=False) for r in range(nsets)]
+    dual = name in W.DUAL_WORKLOADS
+    gen = W.DUAL_WORKLOADS[name] if dual else W.DECODE_WORKLOADS[name]
+    sets = [gen(rep=r, with_latents=False) for r in range(nsets)]
     wl = sets[0]
-    log(f"{name}: {nsets} sets generated in {time.time() - t_gen:.1f}s; pool "
-        f"{wl.num_slots} slots = {wl.num_slots * 352 / 1e9:.2f} GB")
-    cache = fill_pool(lib, W, wl, dev)
+    pools = [wl.primary, wl.extra_pool] if dual else [wl]
+    log(f"{name}: {nsets} sets generated in {time.time() - t_gen:.1f}s; pools "
+        + ", ".join(f"{p.num_slots} slots in {p.block_size}-token pages = "
+                    f"{p.num_slots * 352 / 1e9:.2f} GB" for p in pools))
+    caches = [fill_pool(lib, W, wl.config_id, p.num_blocks, p.block_size,
+                        1000 * (i + 1) + wl.config_id, dev) for i, p in enumerate(pools)]
+    cache = caches[0]
     rows = wl.batch * wl.s_q
     splits = force_splits or lib.plan(wl.batch, wl.s_q, wl.h_q, wl.topk)
     ws_bytes = lib.workspace_size(wl.batch, wl.s_q, wl.h_q, wl.topk, splits)
@@ -146,13 +165,20 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         nl, nr = W.latents(wl.config_id, rows, rep=100 + r)
         inp.append(dict(q=s.q.to(dev), idx=torch.from_numpy(s.indices).to(dev),
                         lat=nl.to(dev), rope=nr.to(dev)))
+        if dual:
+            inp[-1]["idx1"] = torch.from_numpy(s.extra_indices).to(dev)
 
     def append(r):
         lib.quantize_append(inp[r]["lat"], inp[r]["rope"], new_slots, cache)
 
     def decode(r):
-        lib.sparse_decode(inp[r]["q"], cache, inp[r]["idx"], wl.softmax_scale, sink=sink,
-                          num_splits=splits, workspace=ws, out=out, lse=lse)
+        if dual:
+            lib.sparse_decode_dual(inp[r]["q"], caches[0], inp[r]["idx"], caches[1],
+                                   inp[r]["idx1"], wl.softmax_scale, sink=sink,
+                                   num_splits=splits, workspace=ws, out=out, lse=lse)
+        else:
+            lib.sparse_decode(inp[r]["q"], cache, inp[r]["idx"], wl.softmax_scale, sink=sink,
+                              num_splits=splits, workspace=ws, out=out, lse=lse)
 
     # eager reference outputs, then graphs checked against them
     ref = []
@@ -226,7 +252,7 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         f"({100 * res['mfma_frac']:.1f}% MFMA), KV {res['decode_kv_gbps']:.0f} GB/s, "
         f"compulsory {res['decode_hbm_gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
         f"splits {splits}")
-    del cache, ws, inp, g_app, g_dec
+    del cache, caches, ws, inp, g_app, g_dec
     torch.cuda.empty_cache()
     return res
 
@@ -348,7 +374,7 @@ def main():
     head = bench_decode(lib, W, args.workload, args.steps, args.warmup, args.sets, use_graph, dev)
     extra = {}
     if not args.no_extra:
-        for name in ("decode_h16_mtp", "decode_h128_varlen"):
+        for name in ("decode_h16_mtp", "decode_h16_mtp_dual", "decode_h128_varlen"):
             if name != args.workload:
                 extra[name] = bench_decode(lib, W, name, max(20, args.steps // 2),
                                            max(5, args.warmup // 2), args.sets, use_graph, dev)

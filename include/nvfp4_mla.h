@@ -12,7 +12,8 @@
  *     dequantizes them to bf16, and computes softmax(scale * Q K^T) V over all
  *     heads sharing the latent, with an optional per-head attention sink;
  *     d_qk = 576, d_v = 512 (FlashMLA PR #18, PR description).  Returns O and
- *     the log-sum-exp LSE.
+ *     the log-sum-exp LSE.  The dual-cache form attends over two lists in two
+ *     caches with one softmax.
  *   - combine: LSE-weighted merge of split-KV partial results.
  *   - dequantize-gather: the decode's own dequantization, exported so its
  *     bf16 output can be checked bit for bit.
@@ -154,8 +155,10 @@ int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q,
  * Returns 0 and sets the error on invalid arguments.
  *
  * The workspace holds the splits' partial O and LSE and one arrival counter
- * per (query row, group of 16 heads); the last split to finish merges the
- * partials inside the decode kernel.  The caller zero-fills a workspace
+ * per (query row, group of 16 heads).  When h_q is a multiple of 32 a
+ * combine kernel launched right after the decode merges the partials;
+ * otherwise the last split to finish merges them inside the decode kernel
+ * (the counters serve that).  The caller zero-fills a workspace
  * before its first use with a given (batch, s_q, h_q, num_splits); every
  * completed decode leaves the counters zero again, so further decodes of
  * that shape reuse it without clearing (a different shape needs a fresh
@@ -187,7 +190,8 @@ size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
  *              bytes (may be NULL when that size is 0); 256-byte aligned
  *   num_splits 0 = planner's choice, else 1..NVFP4_MLA_MAX_SPLITS
  * h_q must be a multiple of 16 (1..16 * 16), topk in [1, 65536].
- * The whole decode, including the split-KV merge, is one kernel launch.
+ * The decode is one kernel launch, plus one combine launch when h_q is a
+ * multiple of 32 and more than one split runs.
  */
 int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int64_t num_blocks, int32_t block_size,
@@ -197,6 +201,45 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             float softmax_scale, void* out_bf16, float* lse,
                             void* workspace, size_t workspace_bytes,
                             int32_t num_splits, void* stream);
+
+/*
+ * Dual-cache sparse decode: the same attention as nvfp4_mla_sparse_decode,
+ * with one softmax (and the sink applied once) over the union of two top-k
+ * lists that index two different paged caches: the primary cache (the
+ * sliding window, 64-token pages in the pages' setup) and an extra cache (the
+ * indexer's top-k, 2- or 64-token pages).  Each list holds slot ids of its
+ * own cache; the caches may differ in block_size and block_stride_bytes
+ * (sglang PR #38646 "[SM120] opt-in NVFP4 sparse-MLA KV cache format for
+ * DeepSeek-V4": Modifications, the pool's page sizes; Performance, primary
+ * top-k 128 plus extra top-k 512).  The result equals
+ * nvfp4_mla_sparse_decode over one cache holding both pools' records, with
+ * the two lists concatenated (primary first).
+ *
+ *   indices        [batch, s_q, topk] int32 slot ids of kv_cache, < 0 or
+ *                  >= num_blocks*block_size = invalid
+ *   extra_indices  [batch, s_q, extra_topk] int32 slot ids of extra_kv_cache,
+ *                  the same invalid rule against its own slot count
+ *   topk, extra_topk >= 0 with topk + extra_topk in [1, 65536]; a list whose
+ *                  top-k is 0 may be NULL.  Both caches must be valid
+ *                  (checked as for nvfp4_mla_sparse_decode) even when a list
+ *                  is empty.
+ * Every other argument is as for nvfp4_mla_sparse_decode.  The split planner
+ * and the workspace size are those of a single-cache decode with
+ * topk + extra_topk: call nvfp4_mla_sparse_decode_plan and
+ * nvfp4_mla_sparse_decode_workspace_size with that sum.
+ */
+int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache,
+                                 int64_t num_blocks, int32_t block_size,
+                                 int64_t block_stride_bytes, const int32_t* indices,
+                                 int32_t topk, const uint8_t* extra_kv_cache,
+                                 int64_t extra_num_blocks, int32_t extra_block_size,
+                                 int64_t extra_block_stride_bytes,
+                                 const int32_t* extra_indices, int32_t extra_topk,
+                                 int32_t batch, int32_t s_q, int32_t h_q,
+                                 const float* attn_sink, float softmax_scale,
+                                 void* out_bf16, float* lse, void* workspace,
+                                 size_t workspace_bytes, int32_t num_splits,
+                                 void* stream);
 
 /*
  * Split-KV combine.  Given num_splits sink-free partial results over

@@ -17,6 +17,12 @@ attention sink; every query head attends to the same latent):
   the sink, so partial results over disjoint index sets can be merged first and
   the sink applied once afterwards.
 
+Dual-cache decode ([sglang-38646] Modifications: the pool keeps a primary
+cache and an extra cache with their own page sizes, and slot ids are those of
+each cache; Performance: one attention over primary top-k 128 plus extra top-k
+512): the same definition over the joined list of a primary list (rows of the
+primary records) followed by an extra list (rows of the extra records).
+
 Split-KV combine (LSE-weighted merge of partial results over disjoint index
 subsets): LSE = ln sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) O_i divided
 by (1 + exp(sink - LSE)) when a sink is given; all LSE_i = -inf gives O = 0,
@@ -64,6 +70,25 @@ def sparse_decode(q, records, idx, softmax_scale, sink=None):
                 denom = denom + np.exp(np.asarray(sink, dtype=np.float64) - m)
             out[b, s] = (e @ v) / denom[:, None]
     return out, lse
+
+
+def sparse_decode_dual(q, records, idx, extra_records, extra_idx, softmax_scale, sink=None):
+    """Reference dual-cache decode.
+
+    records, idx:             primary records [R0, 352] and row numbers [B, S, topk0]
+    extra_records, extra_idx: extra records [R1, 352] and row numbers [B, S, topk1]
+    Every valid entry of either list is one token of a single softmax (sink
+    once): sparse_decode over the records of both caches stacked, with the
+    extra list's row numbers moved past the primary records.
+    """
+    records = np.asarray(records, dtype=np.uint8).reshape(-1, 352)
+    extra_records = np.asarray(extra_records, dtype=np.uint8).reshape(-1, 352)
+    idx = np.asarray(idx).astype(np.int64)
+    extra_idx = np.asarray(extra_idx).astype(np.int64)
+    joined_idx = np.concatenate(
+        [idx, np.where(extra_idx >= 0, extra_idx + records.shape[0], -1)], axis=-1)
+    joined = np.concatenate([records, extra_records], axis=0)
+    return sparse_decode(q, joined, joined_idx, softmax_scale, sink=sink)
 
 
 def partial_decode(q, records, idx, softmax_scale):

@@ -48,6 +48,10 @@ SIGNATURES = {
     "nvfp4_mla_sparse_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "nvfp4_mla_sparse_decode": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32, _I32, _I32,
                                                _I32, _P, _F32, _P, _P, _P, _SZ, _I32, _P]),
+    "nvfp4_mla_sparse_decode_dual": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32,
+                                                    _P, _I64, _I32, _I64, _P, _I32,
+                                                    _I32, _I32, _I32, _P, _F32, _P, _P, _P, _SZ,
+                                                    _I32, _P]),
     "nvfp4_mla_combine": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _P, _P, _P, _P]),
 }
 
@@ -205,6 +209,46 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
     _check("nvfp4_mla_sparse_decode", code)
+    return out, lse
+
+
+def _index_list(indices, b, s, what):
+    if (indices.dtype != torch.int32 or indices.dim() != 3 or tuple(indices.shape[:2]) != (b, s)
+            or not indices.is_contiguous()):
+        raise ValueError(f"{what} must be a contiguous int32 [B, S_q, topk] tensor")
+    return indices.shape[2]
+
+
+def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, softmax_scale,
+                       sink=None, num_splits=0, workspace=None, out=None, lse=None):
+    """Dual-cache sparse MLA decode: one softmax over `indices` (slot ids of
+    kv_cache) and `extra_indices` (slot ids of extra_kv_cache), each cache
+    with its own page size.  Shapes as for sparse_decode; either list may have
+    top-k 0.  Returns (O bf16 [B, S_q, H, 512], LSE float32 [B, S_q, H])."""
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[-1] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, S_q, H, 576] tensor")
+    b, s, h, _ = q.shape
+    topk0 = _index_list(indices, b, s, "indices")
+    topk1 = _index_list(extra_indices, b, s, "extra_indices")
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
+        raise ValueError("sink must be float32 [H]")
+    if num_splits == 0:
+        num_splits = plan(b, s, h, topk0 + topk1)
+    need = workspace_size(b, s, h, topk0 + topk1, num_splits)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, s, h), dtype=torch.float32, device=q.device)
+    nb0, bs0, st0 = _cache_geometry(kv_cache)
+    nb1, bs1, st1 = _cache_geometry(extra_kv_cache)
+    code = lib().nvfp4_mla_sparse_decode_dual(
+        _ptr(q), _ptr(kv_cache), nb0, bs0, st0, _ptr(indices) if topk0 else None, topk0,
+        _ptr(extra_kv_cache), nb1, bs1, st1, _ptr(extra_indices) if topk1 else None, topk1,
+        b, s, h, _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
+    _check("nvfp4_mla_sparse_decode_dual", code)
     return out, lse
 
 

@@ -218,6 +218,105 @@ int quantize_append_impl(const char* fn, const void* latent_bf16, int64_t latent
   return ok();
 }
 
+// Shared by the single- and dual-cache exports.  `extra` is null for the
+// single-cache decode; topk0 is the primary list's length, topk the joined
+// list's.
+struct ExtraCache {
+  const uint8_t* kv_cache;
+  int64_t num_blocks;
+  int32_t block_size;
+  int64_t block_stride_bytes;
+  const int32_t* indices;
+  int32_t topk;
+};
+
+int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cache,
+                       int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
+                       const int32_t* indices, int32_t topk0, const ExtraCache* extra,
+                       int32_t batch, int32_t s_q, int32_t h_q, const float* attn_sink,
+                       float softmax_scale, void* out_bf16, float* lse, void* workspace,
+                       size_t workspace_bytes_in, int32_t num_splits, void* stream) {
+  if (extra && (topk0 < 0 || extra->topk < 0 || topk0 > 65536 || extra->topk > 65536))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d and extra_topk = %d must be >= 0",
+                topk0, extra ? extra->topk : 0);
+  const int32_t topk = topk0 + (extra ? extra->topk : 0);
+  int rc = check_decode_shape(batch, s_q, h_q, topk);
+  if (rc) return rc;
+  int64_t num_slots = 0, num_slots1 = 0;
+  rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  if (rc) return rc;
+  if (extra) {
+    rc = check_cache(extra->kv_cache, extra->num_blocks, extra->block_size,
+                     extra->block_stride_bytes, &num_slots1);
+    if (rc) return fail(rc, "extra cache: %s", g_last_error.c_str());
+  }
+  if (num_splits < 0 || num_splits > NVFP4_MLA_MAX_SPLITS)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d out of [0, %d]", num_splits,
+                NVFP4_MLA_MAX_SPLITS);
+  if (!std::isfinite(softmax_scale))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  const int64_t rows = (int64_t)batch * s_q;
+  if (rows > 0) {
+    if (!q_bf16 || !out_bf16 || !lse)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "q, indices, out and lse must be non-NULL");
+    if ((topk0 > 0 && !indices) || (extra && extra->topk > 0 && !extra->indices))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "q, indices, out and lse must be non-NULL (an index list may be NULL only "
+                  "when its top-k is 0)");
+    if (!aligned(q_bf16, 16) || !aligned(out_bf16, 16) || !aligned(lse, 4) ||
+        !aligned(indices, 4) || (extra && !aligned(extra->indices, 4)) ||
+        (attn_sink && !aligned(attn_sink, 4)))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "q and out must be 16-byte aligned; indices, lse, sink 4-byte aligned");
+  }
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+  int splits = num_splits == 0 ? plan_splits((int32_t)rows, h_q, topk, cus) : num_splits;
+  const size_t need = workspace_bytes(rows, h_q, splits);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes_in < need)
+      return fail(NVFP4_MLA_ERR_WORKSPACE_TOO_SMALL,
+                  "decode with %d splits needs %zu workspace bytes, got %zu", splits, need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes_in);
+    if (!aligned(workspace, 256))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+  if (rows == 0) return ok();
+  nvfp4::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.cache = kv_cache;
+  a.pa = make_page_addr(block_size, block_stride_bytes);
+  a.num_slots = num_slots;
+  a.indices = indices;
+  a.topk0 = topk0;
+  if (extra) {
+    a.cache1 = extra->kv_cache;
+    a.pa1 = make_page_addr(extra->block_size, extra->block_stride_bytes);
+    a.num_slots1 = num_slots1;
+    a.indices1 = extra->indices;
+  }
+  a.rows = (int32_t)rows;
+  a.h_q = h_q;
+  a.topk = topk;
+  a.sink = attn_sink;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.lse = lse;
+  a.splits = splits;
+  if (splits > 1) {
+    const WsLayout w = ws_layout(rows, h_q, splits);
+    char* base = static_cast<char*>(workspace);
+    a.o_part = reinterpret_cast<float*>(base + w.o_off);
+    a.lse_part = reinterpret_cast<float*>(base + w.lse_off);
+    a.counters = reinterpret_cast<uint32_t*>(base + w.cnt_off);
+  }
+  hipError_t e = nvfp4::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,64 +419,28 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache, int64_t
                             int32_t topk, const float* attn_sink, float softmax_scale,
                             void* out_bf16, float* lse, void* workspace, size_t workspace_bytes_in,
                             int32_t num_splits, void* stream) {
-  int rc = check_decode_shape(batch, s_q, h_q, topk);
-  if (rc) return rc;
-  int64_t num_slots = 0;
-  rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
-  if (rc) return rc;
-  if (num_splits < 0 || num_splits > NVFP4_MLA_MAX_SPLITS)
-    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d out of [0, %d]", num_splits,
-                NVFP4_MLA_MAX_SPLITS);
-  if (!std::isfinite(softmax_scale))
-    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  const int64_t rows = (int64_t)batch * s_q;
-  if (rows > 0) {
-    if (!q_bf16 || !indices || !out_bf16 || !lse)
-      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "q, indices, out and lse must be non-NULL");
-    if (!aligned(q_bf16, 16) || !aligned(out_bf16, 16) || !aligned(lse, 4) ||
-        !aligned(indices, 4) || (attn_sink && !aligned(attn_sink, 4)))
-      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
-                  "q and out must be 16-byte aligned; indices, lse, sink 4-byte aligned");
-  }
-  int cus = 0;
-  rc = check_device(&cus);
-  if (rc) return rc;
-  int splits = num_splits == 0 ? plan_splits((int32_t)rows, h_q, topk, cus) : num_splits;
-  const size_t need = workspace_bytes(rows, h_q, splits);
-  if (need > 0) {
-    if (workspace == nullptr || workspace_bytes_in < need)
-      return fail(NVFP4_MLA_ERR_WORKSPACE_TOO_SMALL,
-                  "decode with %d splits needs %zu workspace bytes, got %zu", splits, need,
-                  workspace == nullptr ? (size_t)0 : workspace_bytes_in);
-    if (!aligned(workspace, 256))
-      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  }
-  if (rows == 0) return ok();
-  nvfp4::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q_bf16);
-  a.cache = kv_cache;
-  a.pa = make_page_addr(block_size, block_stride_bytes);
-  a.num_slots = num_slots;
-  a.indices = indices;
-  a.rows = (int32_t)rows;
-  a.h_q = h_q;
-  a.topk = topk;
-  a.sink = attn_sink;
-  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  a.out = static_cast<uint16_t*>(out_bf16);
-  a.lse = lse;
-  a.splits = splits;
-  if (splits > 1) {
-    const WsLayout w = ws_layout(rows, h_q, splits);
-    char* base = static_cast<char*>(workspace);
-    a.o_part = reinterpret_cast<float*>(base + w.o_off);
-    a.lse_part = reinterpret_cast<float*>(base + w.lse_off);
-    a.counters = reinterpret_cast<uint32_t*>(base + w.cnt_off);
-  }
-  hipError_t e = nvfp4::launch_decode(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess)
-    return fail(NVFP4_MLA_ERR_HIP, "sparse_decode launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return sparse_decode_impl("sparse_decode", q_bf16, kv_cache, num_blocks, block_size,
+                            block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
+                            attn_sink, softmax_scale, out_bf16, lse, workspace,
+                            workspace_bytes_in, num_splits, stream);
+}
+
+int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache, int64_t num_blocks,
+                                 int32_t block_size, int64_t block_stride_bytes,
+                                 const int32_t* indices, int32_t topk,
+                                 const uint8_t* extra_kv_cache, int64_t extra_num_blocks,
+                                 int32_t extra_block_size, int64_t extra_block_stride_bytes,
+                                 const int32_t* extra_indices, int32_t extra_topk, int32_t batch,
+                                 int32_t s_q, int32_t h_q, const float* attn_sink,
+                                 float softmax_scale, void* out_bf16, float* lse,
+                                 void* workspace, size_t workspace_bytes_in, int32_t num_splits,
+                                 void* stream) {
+  const ExtraCache extra{extra_kv_cache, extra_num_blocks, extra_block_size,
+                         extra_block_stride_bytes, extra_indices, extra_topk};
+  return sparse_decode_impl("sparse_decode_dual", q_bf16, kv_cache, num_blocks, block_size,
+                            block_stride_bytes, indices, topk, &extra, batch, s_q, h_q,
+                            attn_sink, softmax_scale, out_bf16, lse, workspace,
+                            workspace_bytes_in, num_splits, stream);
 }
 
 int nvfp4_mla_combine(const float* o_partial, const float* lse_partial, int32_t num_splits,

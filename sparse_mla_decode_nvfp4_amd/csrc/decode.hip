@@ -39,6 +39,7 @@
 
 #include "combine_math.h"
 #include "device_common.h"
+#include "kv_source.h"
 #include "launch.h"
 
 namespace nvfp4 {
@@ -103,18 +104,6 @@ __device__ __forceinline__ void load_tok(RawTok& t, const uint8_t* rec, int g) {
   t.rope = *reinterpret_cast<const u32x4*>(rec + kRopeOffset + 16 * g);
 }
 
-__device__ __forceinline__ int32_t load_idx(const int32_t* idx_row, int p, int t1) {
-  const int32_t v = idx_row[min(p, max(t1 - 1, 0))];   // in bounds: topk >= 1
-  return p < t1 ? v : -1;
-}
-
-__device__ __forceinline__ bool idx_valid(int32_t idx, int64_t num_slots) {
-  return idx >= 0 && (int64_t)idx < num_slots;
-}
-
-__device__ __forceinline__ const uint8_t* rec_ptr(const DecodeArgs& a, int32_t idx) {
-  return a.cache + (idx_valid(idx, a.num_slots) ? a.pa.offset((uint32_t)idx) : 0);
-}
 
 // Eight E2M1 codes times a block scale -> eight fp16, exact: the fp4 convert
 // applies the scale's power of two, F (the scale's mantissa as fp16) the rest.
@@ -150,6 +139,7 @@ __device__ __forceinline__ h16x8 rope8_f16(uint32_t x, uint32_t y) {
 //   ks 16, 17 cover RoPE dims 16g + 8*(ks-16) + [0,8).  Q is laid out to match.
 //   PV (16x16x32): A = P[head n][token 32ks+8g+i], B = V[token 32ks+8g+i][dv],
 //   C = O[head 4g+r][dv 128w + 16nb + n].
+template <bool kDual>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 decode_tile16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * kVChunk];
@@ -177,16 +167,23 @@ decode_tile16_kernel(DecodeArgs a) {
   const int tile0 = split * tiles_per_split;
   const int tile1 = min(ntiles_total, tile0 + tiles_per_split);
   const int t_end = min(a.topk, tile1 * kTile);       // first token past the split
-  const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+  const RowSource<kDual> src(a, row);
   const int my_tok = 16 * wave + n;                    // this lane's token within a tile
+  // raw index of this lane's token of tile t (clamped in bounds: topk >= 1)
+  auto load_idx = [&](int t) { return src.load(min(t * kTile + my_tok, a.topk - 1)); };
+  auto resolve = [&](int32_t v, int t) {
+    const int p = t * kTile + my_tok;
+    return resolve_rec<kDual>(a, v, p < t_end, p, src.topk0);
+  };
 
   // ---- prologue: indices of tiles 0 and 1, token bytes of tile 0 (before
   // the Q set-up, which hides part of their latency)
   int tile = tile0;
-  int32_t idx_cur = load_idx(idx_row, tile * kTile + my_tok, t_end);
-  int32_t idx_nxt = load_idx(idx_row, (tile + 1) * kTile + my_tok, t_end);
+  const RecRef r0 = resolve(load_idx(tile), tile);
+  bool ok_cur = r0.ok;             // this lane's token of the current tile takes part
+  int32_t idx_nxt = load_idx(tile + 1);
   RawTok cur;
-  load_tok(cur, rec_ptr(a, idx_cur), g);
+  load_tok(cur, r0.ptr, g);
 
   // ---- Q^T operand registers (head n, k-chunk g) in fp16 with a per-head
   // power-of-two scale; a negative softmax scale flips Q's sign (exact), so
@@ -249,12 +246,13 @@ decode_tile16_kernel(DecodeArgs a) {
   // bytes are never copied.
   auto step = [&](RawTok& cur, RawTok& nxt, int t) {
     // ---- prefetch: indices two tiles ahead, token bytes one tile ahead
-    const int32_t idx_nn = load_idx(idx_row, (t + 2) * kTile + my_tok, t_end);
-    load_tok(nxt, rec_ptr(a, idx_nxt), g);
+    const int32_t idx_nn = load_idx(t + 2);
+    const RecRef rn = resolve(idx_nxt, t + 1);
+    load_tok(nxt, rn.ptr, g);
     // keep the prefetch at the top of the step: the scheduler would otherwise
     // sink these loads below the dequant and shorten their lead time
     __builtin_amdgcn_sched_barrier(0);
-    const bool cur_valid = idx_valid(idx_cur, a.num_slots);
+    const bool cur_valid = ok_cur;
     const uint64_t vmask = __ballot(cur_valid);
 
     // all waves are done reading the previous tile's V and P
@@ -345,7 +343,7 @@ decode_tile16_kernel(DecodeArgs a) {
         acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc_o[nb], 0, 0, 0);
       }
     }
-    idx_cur = idx_nxt;
+    ok_cur = rn.ok;
     idx_nxt = idx_nn;
   };
 
@@ -429,7 +427,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   if (decode_uses_w32(a.h_q)) return launch_decode_w32(a, stream);
   const int grid = a.rows * (a.h_q / 16) * a.splits;
-  hipLaunchKernelGGL(decode_tile16_kernel, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  if (a.cache1)
+    hipLaunchKernelGGL(decode_tile16_kernel<true>, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_tile16_kernel<false>, dim3(grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@
 #include <math.h>
 
 #include "device_common.h"
+#include "kv_source.h"
 #include "launch.h"
 
 namespace nvfp4 {
@@ -154,6 +155,7 @@ struct IntC {
 //   C = S^T[token 4g+r][head 16b+n] for head blocks b = 0, 1.
 //   PV (32x32x16): A = P[head tl][token 8kg+i], B = V[token 8kg+i][dv 32nb +
 //   tl], C = O[head acc_row(r, kg)][dv 256hf + 32nb + tl].
+template <bool kDual>
 __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_p[];
   lds_u8* const lds = (lds_u8*)smem_p;
@@ -202,38 +204,34 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   const int c_end = min(nchunks, c_begin + cps);
   const int span = max(c_end - c_begin, 0);
   const int my_n = (span + 3) >> 2;             // the same for all pairs
-  const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+  const RowSource<kDual> src(a, row);
 
-  auto valid = [&](int32_t idx) { return idx >= 0 && (int64_t)idx < a.num_slots; };
-  // index of token n of this pair's i-th chunk: the load is unconditional
-  // (clamped in bounds) and chunk_ok marks the entries that exist; the two
-  // are combined a chunk after the load, so no wait follows it
+  // joined-list position of token n of this pair's i-th chunk
+  auto tok_pos = [&](int i) { return (c_begin + pr + 4 * i) * kChunkP + n; };
+  // its index: the load is unconditional (clamped in bounds) and chunk_ok
+  // marks the entries that exist; the two are combined a chunk after the
+  // load, so no wait follows it
   auto load_idx = [&](int i) -> int32_t {
-    const int ic = min(i, max(my_n - 1, 0));
-    const int pos = (c_begin + pr + 4 * ic) * kChunkP + n;
-    return idx_row[min(pos, a.topk - 1)];
+    return src.load(min(tok_pos(min(i, max(my_n - 1, 0))), a.topk - 1));
   };
   auto chunk_ok = [&](int i) -> bool {
     const int c = c_begin + pr + 4 * i;
     return i < my_n && c < c_end && c * kChunkP + n < a.topk;
   };
-  auto rec_of = [&](int32_t idx) {
-    const uint32_t slot = valid(idx) ? (uint32_t)idx : 0u;
-    return a.cache + a.pa.offset(slot);
-  };
 
   // the first chunk's indices and records are requested before the Q
   // set-up below, which hides part of their latency
   RawP buf;
-  int32_t idx_cur = -1, idx_nxt = -1;
+  bool ok_cur = false;
+  int32_t idx_nxt = -1;
   if (my_n > 0) {
-    idx_cur = load_idx(0);
+    const int32_t idx0 = load_idx(0);
     idx_nxt = load_idx(1);
-    idx_cur = chunk_ok(0) ? idx_cur : -1;
-    const uint8_t* rec = rec_of(idx_cur);
-    load_nope(buf, 0, rec, hf, g);
-    load_nope(buf, 1, rec, hf, g);
-    load_tail(buf, rec, hf, g);
+    const RecRef r = resolve_rec<kDual>(a, idx0, chunk_ok(0), tok_pos(0), src.topk0);
+    ok_cur = r.ok;
+    load_nope(buf, 0, r.ptr, hf, g);
+    load_nope(buf, 1, r.ptr, hf, g);
+    load_tail(buf, r.ptr, hf, g);
   }
 
   // ---- Q^T operands in fp16 with a per-head power-of-two scale.  The waves
@@ -315,17 +313,17 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   }
   const int partner = wave ^ 1;
 
-  // Chunk pos from `cur` (index cur_idx, -1 when absent or invalid), up to
+  // Chunk pos from `cur` (cur_ok: whether this lane's token takes part), up to
   // the partial-S exchange; each raw piece is refilled with the next chunk's
   // bytes (raw index nxt_raw, loaded a chunk earlier) right after its use.
   f32x4 sacc[2];
   uint32_t vm16 = 0;
-  auto pre = [&](RawP& cur, int32_t& cur_idx, int32_t& nxt_raw, int pos) {
+  auto pre = [&](RawP& cur, bool& cur_ok, int32_t& nxt_raw, int pos) {
     const int32_t nxt2_raw = load_idx(pos + 2);
-    const bool v = valid(cur_idx);
+    const bool v = cur_ok;
     vm16 = (uint32_t)(__ballot(v) & 0xFFFFull);
-    const int32_t nxt = chunk_ok(pos + 1) ? nxt_raw : -1;
-    const uint8_t* const rec_next = rec_of(nxt);
+    const RecRef rn = resolve_rec<kDual>(a, nxt_raw, chunk_ok(pos + 1), tok_pos(pos + 1), src.topk0);
+    const uint8_t* const rec_next = rn.ptr;
     // block scales of this lane; zero for an invalid token, so its V row is
     // zero
     float S[4];
@@ -370,7 +368,7 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
         sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qv, sacc[b], 0, 0, 0);
       }
     }
-    cur_idx = nxt;
+    cur_ok = rn.ok;
     nxt_raw = nxt2_raw;
     lds_u8* const xs = xs_all + (pos & 1) * kWavesP * kXsBytes;
 #pragma unroll
@@ -495,7 +493,7 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   }
   if (my_n > 0) {
     for (int pos = 0; pos < my_n; pos++) {
-      pre(buf, idx_cur, idx_nxt, pos);
+      pre(buf, ok_cur, idx_nxt, pos);
       pair_wait(pos);
       post(pos);
     }
@@ -685,17 +683,25 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 
 size_t decode_w32_lds_bytes() { return kLdsBytes; }
 
-hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = a.rows * (a.h_q / 32) * a.splits;
-  const size_t lds = decode_w32_lds_bytes();
+template <bool kDual>
+static hipError_t launch_w32_kernel(const DecodeArgs& a, int grid, size_t lds, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel<kDual>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(decode_w32_kernel, dim3(grid), dim3(64 * kWavesP), lds, stream, a);
+  hipLaunchKernelGGL(decode_w32_kernel<kDual>, dim3(grid), dim3(64 * kWavesP), lds, stream, a);
+  return hipSuccess;
+}
+
+hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
+  const int grid = a.rows * (a.h_q / 32) * a.splits;
+  const size_t lds = decode_w32_lds_bytes();
+  hipError_t e0 = a.cache1 ? launch_w32_kernel<true>(a, grid, lds, stream)
+                           : launch_w32_kernel<false>(a, grid, lds, stream);
+  if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   // split partials are merged by the combine kernel: the launch boundary

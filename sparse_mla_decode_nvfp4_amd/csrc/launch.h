@@ -19,15 +19,25 @@ hipError_t launch_dequantize_gather(const uint8_t* cache, int64_t num_slots, con
                                     const int32_t* slots, int64_t n, uint16_t* out,
                                     hipStream_t stream);
 
+// One decode call.  The joined top-k list of a row has `topk` positions:
+// [0, topk0) are slot ids of `cache` (list `indices`, [rows, topk0]); in the
+// dual-cache decode [topk0, topk) are slot ids of the extra cache `cache1`
+// (list `indices1`, [rows, topk - topk0]), which has its own page geometry.
+// Without an extra cache topk0 == topk and the *1 fields are unused.
 struct DecodeArgs {
   const uint16_t* q;        // [rows, h_q, 576] bf16
   const uint8_t* cache;
   PageAddr pa;
   int64_t num_slots;
-  const int32_t* indices;   // [rows, topk]
+  const int32_t* indices;   // [rows, topk0]
+  const uint8_t* cache1;    // extra cache, or null
+  PageAddr pa1;
+  int64_t num_slots1;
+  const int32_t* indices1;  // [rows, topk - topk0]
+  int32_t topk0;
   int32_t rows;             // batch * s_q
   int32_t h_q;
-  int32_t topk;
+  int32_t topk;             // length of the joined list
   const float* sink;        // [h_q] or null
   float scale_log2;         // softmax_scale * log2(e)
   uint16_t* out;            // [rows, h_q, 512] bf16

@@ -32,8 +32,9 @@ V_DIM = 512
 RECORD_BYTES = 352
 
 
-def _rng(config_id, stream, rep=0):
-    return np.random.default_rng([config_id, stream, rep])
+def _rng(config_id, stream, rep=0, pool=0):
+    # pool > 0 gives the second cache of a dual-cache workload its own draws
+    return np.random.default_rng([config_id, stream, rep] + ([pool] if pool else []))
 
 
 def _bf16(x):
@@ -45,14 +46,14 @@ def channel_scales(config_id):
     return np.exp(r.uniform(np.log(0.1), np.log(4.0), size=NOPE_DIM))
 
 
-def latents(config_id, n, rep=0):
+def latents(config_id, n, rep=0, pool=0):
     """bf16 NoPE [n,512] and RoPE [n,64] latents drawn for n tokens."""
     cs = channel_scales(config_id)
-    r1 = _rng(config_id, 1, rep)
+    r1 = _rng(config_id, 1, rep, pool)
     nope = r1.standard_normal((n, NOPE_DIM)) * cs[None, :]
     outlier = r1.random((n, NOPE_DIM)) < 0.01
     nope = np.where(outlier, nope * 20.0, nope)
-    rope = _rng(config_id, 2, rep).standard_normal((n, ROPE_DIM))
+    rope = _rng(config_id, 2, rep, pool).standard_normal((n, ROPE_DIM))
     return _bf16(nope), _bf16(rope)
 
 
@@ -261,9 +262,105 @@ def append_write(rep=0, num_tokens=16384, num_slots=262144, p_skip=0.10):
                           latent, rope, sm, sentinel)
 
 
+@dataclass
+class PagedPool:
+    """One paged cache of a dual-cache workload: its geometry, and the
+    sorted distinct slots its indices (and new tokens) use with those tokens'
+    latents in that order."""
+    block_size: int
+    num_blocks: int
+    slots: np.ndarray                    # int64 [n] sorted distinct
+    latent: Optional[torch.Tensor]       # bf16 [n, 512] (None: not drawn)
+    rope: Optional[torch.Tensor]         # bf16 [n, 64]
+
+    @property
+    def num_slots(self):
+        return self.num_blocks * self.block_size
+
+    def slot_rows(self, slots):
+        slots = np.asarray(slots, dtype=np.int64)
+        rows = np.searchsorted(self.slots, np.maximum(slots, 0))
+        return np.where(slots < 0, -1, rows)
+
+
+@dataclass
+class DualDecodeWorkload:
+    """One dual-cache decode step: `indices` are slot ids of the primary pool,
+    `extra_indices` slot ids of the extra pool; one softmax covers both.  The
+    step's new tokens (the queries themselves) go to the primary pool."""
+    name: str
+    config_id: int
+    batch: int
+    s_q: int
+    h_q: int
+    softmax_scale: float
+    q: torch.Tensor                      # bf16 [B, S_q, H, 576]
+    sink: Optional[np.ndarray]           # float32 [H]
+    primary: PagedPool
+    extra_pool: PagedPool
+    indices: np.ndarray                  # int32 [B, S_q, topk0]
+    extra_indices: np.ndarray            # int32 [B, S_q, topk1]
+    new_slots: np.ndarray                # int64 [B * S_q], primary slots
+    description: str = ""
+
+    @property
+    def topk(self):
+        return self.indices.shape[2] + self.extra_indices.shape[2]
+
+
+def decode_h16_mtp_dual(rep=0, batch=256, with_latents=True, extra_block_size=2):
+    """The h_q 16 MTP decode with its two index kinds in two caches, as the
+    DeepSeek-V4 pool keeps them: B 256, s_q 2, 16 heads, 65536-token
+    contexts.  Query j sits at position L-2+j.  Primary (sliding-window)
+    cache: each sequence's last 256 positions in four 64-token pages; its list
+    is the 128-token window ending at the query.  Extra cache: the whole
+    history in `extra_block_size`-token pages (2 by default); its list is 512
+    distinct positions drawn from before the window.  3 % of each list
+    invalid; sink."""
+    cid, bs0, seq, s_q, win, extra_k = 5, 64, 65536, 2, 128, 512
+    bs1 = extra_block_size
+    recent = 256                                   # positions the primary pool keeps
+    r6 = _rng(cid, 6, 0)
+    t0, total0 = _page_table(r6, [recent // bs0] * batch)
+    t1, total1 = _page_table(r6, [seq // bs1] * batch)
+    r4 = _rng(cid, 4, rep)
+    idx0 = np.empty((batch, s_q, win), dtype=np.int64)
+    idx1 = np.empty((batch, s_q, extra_k), dtype=np.int64)
+    new_slots = np.empty(batch * s_q, dtype=np.int64)
+    base = seq - recent
+    for b in range(batch):
+        for j in range(s_q):
+            p = seq - s_q + j
+            window = np.arange(p - win + 1, p + 1) - base
+            idx0[b, j] = t0[b][window // bs0] * bs0 + window % bs0
+            hist = r4.choice(p - win + 1, size=extra_k, replace=False)
+            idx1[b, j] = t1[b][hist // bs1] * bs1 + hist % bs1
+            new_slots[b * s_q + j] = t0[b][(p - base) // bs0] * bs0 + (p - base) % bs0
+    idx0[r4.random(idx0.shape) < 0.03] = -1
+    idx1[r4.random(idx1.shape) < 0.03] = -1
+    q = _bf16(_rng(cid, 3, rep).standard_normal((batch, s_q, 16, QK_DIM)))
+    sink = _rng(cid, 5, 0).standard_normal(16).astype(np.float32)
+    slots0 = np.unique(np.concatenate([idx0[idx0 >= 0], new_slots]))
+    slots1 = np.unique(idx1[idx1 >= 0])
+    lat0 = rope0 = lat1 = rope1 = None
+    if with_latents:
+        lat0, rope0 = latents(cid, len(slots0), rep)
+        lat1, rope1 = latents(cid, len(slots1), rep, pool=1)
+    return DualDecodeWorkload(
+        "decode_h16_mtp_dual", cid, batch, s_q, 16, float(np.float32(1.0 / 24.0)), q, sink,
+        PagedPool(bs0, total0, slots0, lat0, rope0), PagedPool(bs1, total1, slots1, lat1, rope1),
+        idx0.astype(np.int32), idx1.astype(np.int32), new_slots,
+        f"h_q 16 MTP dual cache: B{batch} S_q2, 65536-token contexts, primary 128-token "
+        f"window (64-token pages) + extra 512 history ({bs1}-token pages), 3% invalid, sink")
+
+
 DECODE_WORKLOADS = {
     "tiny": tiny,
     "decode_h64": decode_h64,
     "decode_h128_varlen": decode_h128_varlen,
     "decode_h16_mtp": decode_h16_mtp,
+}
+
+DUAL_WORKLOADS = {
+    "decode_h16_mtp_dual": decode_h16_mtp_dual,
 }

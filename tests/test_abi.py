@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = m.lib()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), name
         assert name in m.SIGNATURES, name
@@ -116,6 +116,47 @@ def dec(**kw):
 def test_sparse_decode_rejects_bad_arguments(kw, needle):
     assert dec(**kw) == m.ERR_INVALID_ARGUMENT
     assert needle in m.last_error()
+
+
+def dual(**kw):
+    a = dict(q=P16, cache=P16, nblocks=4, bs=64, stride=64 * 352, idx=P16, topk=128,
+             xcache=P256, xnblocks=100, xbs=2, xstride=2 * 352, xidx=P16, xtopk=512,
+             batch=2, s_q=1, h_q=16, sink=NULL, scale=0.04, out=P16, lse=P16, ws=NULL,
+             ws_bytes=0, splits=1, stream=NULL)
+    a.update(kw)
+    return m.lib().nvfp4_mla_sparse_decode_dual(
+        a["q"], a["cache"], a["nblocks"], a["bs"], a["stride"], a["idx"], a["topk"],
+        a["xcache"], a["xnblocks"], a["xbs"], a["xstride"], a["xidx"], a["xtopk"],
+        a["batch"], a["s_q"], a["h_q"], a["sink"], a["scale"], a["out"], a["lse"], a["ws"],
+        a["ws_bytes"], a["splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw, needle", [
+    (dict(topk=-1), ">= 0"),
+    (dict(xtopk=-5), ">= 0"),
+    (dict(topk=0, xtopk=0), "topk"),
+    (dict(topk=60000, xtopk=6000), "topk"),
+    (dict(xcache=NULL), "extra cache: kv_cache is NULL"),
+    (dict(xstride=2 * 352 + 8), "extra cache"),
+    (dict(xstride=352), "extra cache"),
+    (dict(xbs=0), "extra cache"),
+    (dict(cache=NULL), "kv_cache is NULL"),
+    (dict(idx=NULL), "non-NULL"),
+    (dict(xidx=NULL), "non-NULL"),
+    (dict(xidx=ctypes.c_void_p(0x100002)), "aligned"),
+    (dict(h_q=24), "multiple of 16"),
+    (dict(splits=65), "num_splits"),
+])
+def test_sparse_decode_dual_rejects_bad_arguments(kw, needle):
+    assert dual(**kw) == m.ERR_INVALID_ARGUMENT
+    assert needle in m.last_error()
+
+
+def test_sparse_decode_dual_accepts_an_empty_list_with_a_null_pointer():
+    if torch.cuda.device_count() > 0:
+        pytest.skip("device-gate check is for GPU-less hosts")
+    assert dual(topk=0, idx=NULL) == m.ERR_UNSUPPORTED_DEVICE
+    assert dual(xtopk=0, xidx=NULL) == m.ERR_UNSUPPORTED_DEVICE
 
 
 def test_combine_and_gather_reject_bad_arguments():

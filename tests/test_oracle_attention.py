@@ -1,10 +1,13 @@
-"""Pins of the oracle's sparse decode and split-KV combine.
+"""Pins of the oracle's sparse decode, dual-cache decode and split-KV combine.
 
 Pinned against: torch's scaled_dot_product_attention and logsumexp in float64
 (dense attention over the whole pool is the special case top-k = pool with no
 invalid index and no sink), closed forms (one token, zero query, sink
 algebra, empty rows) and invariants (index order, inserted -1, duplicates,
-splitting then combining).
+splitting then combining).  The dual-cache decode is pinned by a dense
+softmax with the sink as an extra zero-valued logit column, by combining the
+two lists' separate decodes, by moving a token from one cache to the other,
+and by its one-list special cases.
 """
 
 import numpy as np
@@ -119,3 +122,72 @@ def test_split_then_combine_equals_unsplit(tiny, parts):
 def test_combine_of_nothing_is_empty():
     o, l = A.combine(np.zeros((3, 2, 4, 512)), np.full((3, 2, 4), -np.inf), sink=np.zeros(4))
     assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+@pytest.fixture(scope="module")
+def two_pools():
+    """A primary pool of 40 and an extra pool of 30 records, quantized by the
+    oracle from differently seeded latents, and two query rows of 16 heads."""
+    lat0, rope0 = W.latents(0, 40, rep=7)
+    lat1, rope1 = W.latents(0, 30, rep=7, pool=1)
+    r0 = C.quantize_records(lat0.to(torch.float64).numpy(), rope0.to(torch.float64).numpy())
+    r1 = C.quantize_records(lat1.to(torch.float64).numpy(), rope1.to(torch.float64).numpy())
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 2, 16, 576))
+    i0 = np.array([[[3, 9, -1, 39, 0, 12, 3]], [[5, -1, -1, 1, 2, 30, 31]]]).reshape(1, 2, 7)
+    i1 = np.array([[[29, -1, 0, 7, 8]], [[4, 4, 17, -1, 22]]]).reshape(1, 2, 5)
+    sink = np.linspace(-2, 1.5, 16)
+    return r0, r1, q, i0, i1, sink
+
+
+def test_dual_matches_dense_softmax_with_sink_column(two_pools):
+    r0, r1, q, i0, i1, sink = two_pools
+    scale = float(np.float32(1.0 / 24.0))      # the decode's scale is a float32
+    o, lse = A.sparse_decode_dual(q, r0, i0, r1, i1, scale, sink=sink)
+    k0 = torch.from_numpy(C.dequantize_records(r0))
+    k1 = torch.from_numpy(C.dequantize_records(r1))
+    for s in range(2):
+        keys = torch.cat([k0[[t for t in i0[0, s] if t >= 0]], k1[[t for t in i1[0, s] if t >= 0]]])
+        z = scale * (torch.from_numpy(q[0, s]) @ keys.T)                   # [16, n]
+        zs = torch.cat([z, torch.from_numpy(sink)[:, None]], dim=1)        # sink as a logit
+        vals = torch.cat([keys[:, :512], torch.zeros(1, 512, dtype=torch.float64)])
+        ref = torch.softmax(zs, dim=1) @ vals
+        assert np.allclose(o[0, s], ref.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(lse[0, s], torch.logsumexp(z, dim=1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_dual_is_the_combine_of_its_two_lists(two_pools):
+    r0, r1, q, i0, i1, sink = two_pools
+    o, lse = A.sparse_decode_dual(q, r0, i0, r1, i1, 0.07, sink=sink)
+    oa, la = A.partial_decode(q, r0, i0, 0.07)
+    ob, lb = A.partial_decode(q, r1, i1, 0.07)
+    oc, lc = A.combine(np.stack([oa, ob]), np.stack([la, lb]), sink=sink)
+    assert np.allclose(o, oc, atol=1e-12) and np.allclose(lse, lc, atol=1e-12)
+
+
+def test_dual_token_moves_between_caches(two_pools):
+    """A primary entry served from a copy of its record in the extra pool
+    (and the reverse) gives the same result."""
+    r0, r1, q, i0, i1, sink = two_pools
+    o, lse = A.sparse_decode_dual(q, r0, i0, r1, i1, 0.05, sink=sink)
+    # primary entry 39 of row 0 becomes extra row 30 (a copy of primary record 39)
+    r1b = np.concatenate([r1, r0[39:40]])
+    i0b, i1b = i0.copy(), i1.copy()
+    i0b[0, 0, 3] = -1
+    i1b[0, 0, 1] = 30
+    ob, lb = A.sparse_decode_dual(q, r0, i0b, r1b, i1b, 0.05, sink=sink)
+    assert np.allclose(o, ob, atol=1e-12) and np.allclose(lse, lb, atol=1e-12)
+
+
+def test_dual_with_one_empty_list_is_the_plain_decode(two_pools):
+    r0, r1, q, i0, i1, sink = two_pools
+    none = np.zeros((1, 2, 0), dtype=np.int64)
+    o, lse = A.sparse_decode_dual(q, r0, i0, r1, none, 0.05, sink=sink)
+    o0, l0 = A.sparse_decode(q, r0, i0, 0.05, sink=sink)
+    assert np.array_equal(o, o0) and np.array_equal(lse, l0)
+    o, lse = A.sparse_decode_dual(q, r0, none, r1, i1, 0.05, sink=sink)
+    o1, l1 = A.sparse_decode(q, r1, i1, 0.05, sink=sink)
+    assert np.allclose(o, o1, atol=1e-14) and np.allclose(lse, l1, atol=1e-14)
+    allinv = np.full((1, 2, 3), -1)
+    o, lse = A.sparse_decode_dual(q, r0, allinv, r1, allinv, 0.05, sink=sink)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
