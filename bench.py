@@ -103,9 +103,10 @@ def decode_accounting(sets, wl):
             valid = (idx >= 0) & (idx < n_slots)
             nv += int(valid.sum())
             nu += len(np.unique(idx[valid]))
+        rb = getattr(wl, "record_bytes", 352)
         fl.append(nv * FLOP_PER_TOKEN_HEAD * wl.h_q)
-        kv.append(nv * 352)
-        uniq.append(nu * 352)
+        kv.append(nv * rb)
+        uniq.append(nu * rb)
     rows = wl.batch * wl.s_q
     other = (rows * wl.h_q * 576 * 2 + rows * wl.h_q * 512 * 2 + rows * wl.h_q * 4
              + rows * wl.topk * 4 + wl.h_q * 4)
@@ -113,11 +114,11 @@ def decode_accounting(sets, wl):
                 unique_bytes=float(np.mean(uniq)) + other, other_bytes=other)
 
 
-def fill_pool(lib, W, config_id, num_blocks, block_size, seed, dev):
+def fill_pool(lib, W, config_id, num_blocks, block_size, seed, dev, record_bytes=352):
     """A paged cache with every slot holding a record quantized (by the HIP
     append) from seeded random latents of the workload's distribution."""
     import torch
-    cache = lib.new_cache(num_blocks, block_size, dev)
+    cache = lib.new_cache(num_blocks, block_size, dev, record_bytes=record_bytes)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     chunk = 1 << 20
@@ -148,9 +149,10 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     pools = [wl.primary, wl.extra_pool] if dual else [wl]
     log(f"{name}: {nsets} sets generated in {time.time() - t_gen:.1f}s; pools "
         + ", ".join(f"{p.num_slots} slots in {p.block_size}-token pages = "
-                    f"{p.num_slots * 352 / 1e9:.2f} GB" for p in pools))
+                    f"{p.num_slots * getattr(wl, 'record_bytes', 352) / 1e9:.2f} GB" for p in pools))
+    rb = getattr(wl, "record_bytes", 352)
     caches = [fill_pool(lib, W, wl.config_id, p.num_blocks, p.block_size,
-                        1000 * (i + 1) + wl.config_id, dev) for i, p in enumerate(pools)]
+                        1000 * (i + 1) + wl.config_id, dev, rb) for i, p in enumerate(pools)]
     cache = caches[0]
     rows = wl.batch * wl.s_q
     splits = force_splits or lib.plan(wl.batch, wl.s_q, wl.h_q, wl.topk)
@@ -374,7 +376,8 @@ def main():
     head = bench_decode(lib, W, args.workload, args.steps, args.warmup, args.sets, use_graph, dev)
     extra = {}
     if not args.no_extra:
-        for name in ("decode_h16_mtp", "decode_h16_mtp_dual", "decode_h128_varlen"):
+        for name in ("decode_h16_mtp", "decode_h16_mtp_dual", "decode_h128_varlen",
+                     "decode_h64_ds_mla"):
             if name != args.workload:
                 extra[name] = bench_decode(lib, W, name, max(20, args.steps // 2),
                                            max(5, args.warmup // 2), args.sets, use_graph, dev)

@@ -24,6 +24,14 @@
  *   [320,352) 32 E4M3 block scales (16 NoPE elements each); the scale of
  *             block s is at byte 320 + 8*(s&3) + (s>>2)
  *
+ * The 432-byte record ("nvfp4_ds_mla", vLLM PR #82, summary and Fix; the
+ * *_ds_mla entry points):
+ *   [0,256)   512 E2M1 NoPE codes, packed as above
+ *   [256,288) 32 E4M3 block scales in block order (block s at byte 256 + s)
+ *   [288,304) zero pad
+ *   [304,432) 64 bf16 RoPE values, copied verbatim from the input
+ * Both records use the same NoPE codes and scales for the same latent.
+ *
  * Conventions for every entry point:
  *   - All pointers are device pointers owned by the caller unless stated
  *     otherwise; the library never allocates, frees or retains them.
@@ -56,6 +64,8 @@ extern "C" {
 #define NVFP4_MLA_ABI_VERSION 1
 
 #define NVFP4_MLA_RECORD_BYTES 352
+/* The 432-byte "nvfp4_ds_mla" record (the *_ds_mla entry points). */
+#define NVFP4_MLA_DS_MLA_RECORD_BYTES 432
 #define NVFP4_MLA_NOPE_DIM 512
 #define NVFP4_MLA_ROPE_DIM 64
 #define NVFP4_MLA_QK_DIM 576
@@ -79,10 +89,11 @@ int nvfp4_mla_abi_version(void);
  * The string is owned by the library and valid until the thread's next call. */
 const char* nvfp4_mla_last_error(void);
 
-/* Checks that record_bytes / nope / rope / v dimensions are the ones this
- * library implements (352 / 512 / 64 / 512) -- the shape-based format
- * dispatch of FlashMLA PR #18 reduced to one format.  Returns NVFP4_MLA_OK or
- * NVFP4_MLA_ERR_UNSUPPORTED_FORMAT.  Host-only; never touches the device. */
+/* Checks that record_bytes / nope / rope / v dimensions are ones this
+ * library implements (352 or 432 / 512 / 64 / 512) -- the shape-based format
+ * dispatch of FlashMLA PR #18 reduced to these two records.  Returns
+ * NVFP4_MLA_OK or NVFP4_MLA_ERR_UNSUPPORTED_FORMAT.  Host-only; never
+ * touches the device. */
 int nvfp4_mla_check_format(int32_t record_bytes, int32_t nope_dim,
                            int32_t rope_dim, int32_t v_dim);
 
@@ -129,6 +140,22 @@ int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_s
                                    void* stream);
 
 /*
+ * Quantize-append into 432-byte "nvfp4_ds_mla" records (layout above): the
+ * NoPE codes and block scales of nvfp4_mla_quantize_append, the scales in
+ * block order, the 16-byte pad zeroed and the bf16 RoPE bits copied verbatim
+ * (vLLM PR #82, Fix and Tests).  Inputs are bf16 only: the record's RoPE lane
+ * is bf16.  block_stride_bytes must be >= block_size * 432.  Every other
+ * argument, layout, alignment rule, skip rule and error is that of
+ * nvfp4_mla_quantize_append.
+ */
+int nvfp4_mla_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row_stride,
+                                     const void* rope_bf16, int64_t rope_row_stride,
+                                     const int64_t* slot_mapping, int64_t num_tokens,
+                                     uint8_t* kv_cache, int64_t num_blocks,
+                                     int32_t block_size, int64_t block_stride_bytes,
+                                     void* stream);
+
+/*
  * Dequantize-gather: out[i, :] = the 576 bf16 values of the record at
  * slots[i] ([512 NoPE = e2m1 * scale | 64 RoPE]), exactly as the decode
  * dequantizes them (every value is exact in bf16).  slots[i] < 0 or beyond
@@ -139,6 +166,14 @@ int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks,
                                 int32_t block_size, int64_t block_stride_bytes,
                                 const int32_t* slots, int64_t n,
                                 void* out_bf16, void* stream);
+
+/* Dequantize-gather over a cache of 432-byte records: NoPE as above, RoPE
+ * the stored bf16 bits.  Arguments and errors as nvfp4_mla_dequantize_gather
+ * (block_stride_bytes >= block_size * 432). */
+int nvfp4_mla_dequantize_gather_ds_mla(const uint8_t* kv_cache, int64_t num_blocks,
+                                       int32_t block_size, int64_t block_stride_bytes,
+                                       const int32_t* slots, int64_t n,
+                                       void* out_bf16, void* stream);
 
 /*
  * Split planner.  Chooses the number of split-KV partitions for a decode of
@@ -203,6 +238,22 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int32_t num_splits, void* stream);
 
 /*
+ * Sparse decode over a cache of 432-byte records: the attention of
+ * nvfp4_mla_sparse_decode, with K the record's dequantized NoPE followed by
+ * its bf16 RoPE.  Arguments, workspace (nvfp4_mla_sparse_decode_plan and
+ * _workspace_size apply unchanged) and errors as nvfp4_mla_sparse_decode;
+ * block_stride_bytes >= block_size * 432.
+ */
+int nvfp4_mla_sparse_decode_ds_mla(const void* q_bf16, const uint8_t* kv_cache,
+                                   int64_t num_blocks, int32_t block_size,
+                                   int64_t block_stride_bytes, const int32_t* indices,
+                                   int32_t batch, int32_t s_q, int32_t h_q,
+                                   int32_t topk, const float* attn_sink,
+                                   float softmax_scale, void* out_bf16, float* lse,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t num_splits, void* stream);
+
+/*
  * Dual-cache sparse decode: the same attention as nvfp4_mla_sparse_decode,
  * with one softmax (and the sink applied once) over the union of two top-k
  * lists that index two different paged caches: the primary cache (the
@@ -240,6 +291,22 @@ int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache,
                                  void* out_bf16, float* lse, void* workspace,
                                  size_t workspace_bytes, int32_t num_splits,
                                  void* stream);
+
+/* Dual-cache sparse decode over two caches of 432-byte records: arguments
+ * and errors as nvfp4_mla_sparse_decode_dual, both caches holding 432-byte
+ * records. */
+int nvfp4_mla_sparse_decode_dual_ds_mla(const void* q_bf16, const uint8_t* kv_cache,
+                                        int64_t num_blocks, int32_t block_size,
+                                        int64_t block_stride_bytes, const int32_t* indices,
+                                        int32_t topk, const uint8_t* extra_kv_cache,
+                                        int64_t extra_num_blocks, int32_t extra_block_size,
+                                        int64_t extra_block_stride_bytes,
+                                        const int32_t* extra_indices, int32_t extra_topk,
+                                        int32_t batch, int32_t s_q, int32_t h_q,
+                                        const float* attn_sink, float softmax_scale,
+                                        void* out_bf16, float* lse, void* workspace,
+                                        size_t workspace_bytes, int32_t num_splits,
+                                        void* stream);
 
 /*
  * Split-KV combine.  Given num_splits sink-free partial results over

@@ -40,7 +40,7 @@ def sparse_decode(q, records, idx, softmax_scale, sink=None):
     """Reference decode.
 
     q:       float64 [B, S, H, 576]
-    records: uint8 [R, 352]  -- the token records the indices refer to
+    records: uint8 [R, 352 or 432]  -- the token records the indices refer to
     idx:     int [B, S, topk] -- row numbers into `records`, < 0 = invalid
     softmax_scale: the float32 scale, used at its exact value
     sink:    float64 [H] or None
@@ -75,14 +75,17 @@ def sparse_decode(q, records, idx, softmax_scale, sink=None):
 def sparse_decode_dual(q, records, idx, extra_records, extra_idx, softmax_scale, sink=None):
     """Reference dual-cache decode.
 
-    records, idx:             primary records [R0, 352] and row numbers [B, S, topk0]
-    extra_records, extra_idx: extra records [R1, 352] and row numbers [B, S, topk1]
-    Every valid entry of either list is one token of a single softmax (sink
-    once): sparse_decode over the records of both caches stacked, with the
-    extra list's row numbers moved past the primary records.
+    records, idx:             primary records [R0, W] and row numbers [B, S, topk0]
+    extra_records, extra_idx: extra records [R1, W] and row numbers [B, S, topk1]
+    (W = 352 or 432, the same for both).  Every valid entry of either list is
+    one token of a single softmax (sink once): sparse_decode over the records
+    of both caches stacked, with the extra list's row numbers moved past the
+    primary records.
     """
-    records = np.asarray(records, dtype=np.uint8).reshape(-1, 352)
-    extra_records = np.asarray(extra_records, dtype=np.uint8).reshape(-1, 352)
+    records = np.asarray(records, dtype=np.uint8)
+    extra_records = np.asarray(extra_records, dtype=np.uint8)
+    assert records.ndim == 2 and extra_records.ndim == 2
+    assert records.shape[1] == extra_records.shape[1], "one record format for both caches"
     idx = np.asarray(idx).astype(np.int64)
     extra_idx = np.asarray(extra_idx).astype(np.int64)
     joined_idx = np.concatenate(

@@ -1,4 +1,5 @@
-"""Element encodings and the 352-byte token record, restated from the pages.
+"""Element encodings and the 352- and 432-byte token records, restated from
+the pages.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -9,6 +10,13 @@ Record layout ("nvfp4.fp8rope", [FlashMLA-18] PR description):
                     the scale of element block s sits at byte 8*(s&3) + (s>>2)
                     of this area (an 8x4 -> 4x8 transpose).
 
+Record layout ("nvfp4_ds_mla", 432 bytes, [vLLM-82] summary and Fix: 256 B
+FP4 NoPE + 32 B E4M3 scales + 16 B alignment pad + 128 B BF16 RoPE):
+  bytes [0, 256)    the same 512 E2M1 NoPE codes
+  bytes [256, 288)  32 E4M3 block scales
+  bytes [288, 304)  zero pad
+  bytes [304, 432)  64 bf16 RoPE values, the input's 16-bit pattern verbatim
+
 Readings where the page is silent (each listed in the design notes):
   * Nibble order of "packed 2/byte": element 2j is the LOW nibble of byte j,
     element 2j+1 the high nibble.
@@ -16,6 +24,10 @@ Readings where the page is silent (each listed in the design notes):
     all-ones pattern 0x7F/0xFF is NaN, largest finite 448.
   * Rounding to either grid is round-to-nearest, ties to the even code, on the
     finite grid; magnitudes beyond the largest finite value saturate to it.
+  * The 432-byte record's regions lie in the order the page lists them; its
+    scales are in block order (the page names no permutation for it); its
+    NoPE bytes pack nibbles as the 352-byte record does; bf16 is stored
+    little-endian.
 
 Every decoder is written from the bit fields; the grids used for encoding are
 produced by those decoders.  Encoding never divides: "nearest to a/b" is
@@ -37,6 +49,13 @@ NOPE_BYTES = NOPE_DIM // 2         # 256
 ROPE_OFFSET = NOPE_OFFSET + NOPE_BYTES   # 256
 SCALE_OFFSET = ROPE_OFFSET + ROPE_DIM    # 320
 RECORD_BYTES = SCALE_OFFSET + N_GROUPS   # 352
+
+# the 432-byte "nvfp4_ds_mla" record
+DS_SCALE_OFFSET = NOPE_OFFSET + NOPE_BYTES       # 256
+DS_PAD_OFFSET = DS_SCALE_OFFSET + N_GROUPS       # 288
+DS_PAD_BYTES = 16
+DS_ROPE_OFFSET = DS_PAD_OFFSET + DS_PAD_BYTES    # 304
+DS_RECORD_BYTES = DS_ROPE_OFFSET + 2 * ROPE_DIM  # 432
 
 E2M1_MAX = 6.0
 
@@ -132,3 +151,26 @@ def e4m3_encode_satfinite(x):
     assert np.all(np.isfinite(x)), "E4M3 encode needs finite input"
     mag = nearest_code(np.abs(x), 1.0, E4M3_GRID)
     return (np.signbit(x).astype(np.int64) << 7 | mag).astype(np.uint8)
+
+
+def bf16_decode(bits):
+    """Value of bfloat16 bit patterns (uint16), from the fields: sign, 8-bit
+    exponent (bias 127), 7-bit fraction; exponent 255 gives inf/NaN."""
+    b = np.asarray(bits).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = (b & 0x7F).astype(np.float64)
+    with np.errstate(over="ignore"):
+        mag = np.where(e == 0, f * 2.0 ** -133, (1.0 + f / 128.0) * np.exp2(e - 127.0))
+    mag = np.where(e == 255, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def bf16_bits(x):
+    """bfloat16 bit patterns of values that bfloat16 represents exactly (the
+    16-bit inputs of the write path); anything else is an error."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64), equal_nan=True)
+    u = x32.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "not a bfloat16 value"
+    return (u >> 16).astype(np.uint16)

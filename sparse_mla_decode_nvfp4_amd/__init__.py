@@ -17,7 +17,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnvfp4_mla.so")
 
-RECORD_BYTES = 352
+RECORD_BYTES = 352            # "nvfp4.fp8rope" record
+DS_MLA_RECORD_BYTES = 432     # "nvfp4_ds_mla" record (the *_ds_mla exports)
 NOPE_DIM = 512
 ROPE_DIM = 64
 QK_DIM = 576
@@ -52,6 +53,17 @@ SIGNATURES = {
                                                     _P, _I64, _I32, _I64, _P, _I32,
                                                     _I32, _I32, _I32, _P, _F32, _P, _P, _P, _SZ,
                                                     _I32, _P]),
+    "nvfp4_mla_quantize_append_ds_mla": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P,
+                                                        _I64, _I32, _I64, _P]),
+    "nvfp4_mla_dequantize_gather_ds_mla": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _I64, _P,
+                                                          _P]),
+    "nvfp4_mla_sparse_decode_ds_mla": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32, _I32,
+                                                      _I32, _I32, _P, _F32, _P, _P, _P, _SZ,
+                                                      _I32, _P]),
+    "nvfp4_mla_sparse_decode_dual_ds_mla": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32,
+                                                           _P, _I64, _I32, _I64, _P, _I32,
+                                                           _I32, _I32, _I32, _P, _F32, _P, _P,
+                                                           _P, _SZ, _I32, _P]),
     "nvfp4_mla_combine": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _P, _P, _P, _P]),
 }
 
@@ -112,17 +124,28 @@ def _ptr(t):
 
 def _cache_geometry(kv_cache):
     """(num_blocks, block_size, block_stride_bytes) of a [blocks, block_size,
-    352] uint8 cache tensor (pages may be padded: stride(0) >= block_size*352)."""
-    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 3 or kv_cache.shape[2] != RECORD_BYTES:
-        raise ValueError("kv_cache must be a uint8 tensor [num_blocks, block_size, 352]")
-    if kv_cache.stride(2) != 1 or kv_cache.stride(1) != RECORD_BYTES:
-        raise ValueError("records within a page must be contiguous 352-byte rows")
+    R] uint8 cache tensor, R = 352 or 432 (pages may be padded: stride(0) >=
+    block_size * R)."""
+    if (kv_cache.dtype != torch.uint8 or kv_cache.dim() != 3
+            or kv_cache.shape[2] not in (RECORD_BYTES, DS_MLA_RECORD_BYTES)):
+        raise ValueError("kv_cache must be a uint8 tensor [num_blocks, block_size, 352 or 432]")
+    r = kv_cache.shape[2]
+    if kv_cache.stride(2) != 1 or kv_cache.stride(1) != r:
+        raise ValueError(f"records within a page must be contiguous {r}-byte rows")
     return kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0)
 
 
-def new_cache(num_blocks, block_size, device="cuda", fill=0):
-    """A zero-filled (or `fill`-filled) paged cache [num_blocks, block_size, 352]."""
-    return torch.full((num_blocks, block_size, RECORD_BYTES), fill, dtype=torch.uint8,
+def _ds(kv_cache):
+    """Export-name suffix for the cache's record: '' or '_ds_mla'."""
+    return "_ds_mla" if kv_cache.shape[2] == DS_MLA_RECORD_BYTES else ""
+
+
+def new_cache(num_blocks, block_size, device="cuda", fill=0, record_bytes=RECORD_BYTES):
+    """A zero-filled (or `fill`-filled) paged cache [num_blocks, block_size,
+    record_bytes] (352 or 432)."""
+    if record_bytes not in (RECORD_BYTES, DS_MLA_RECORD_BYTES):
+        raise ValueError("record_bytes must be 352 or 432")
+    return torch.full((num_blocks, block_size, record_bytes), fill, dtype=torch.uint8,
                       device=device)
 
 
@@ -131,7 +154,7 @@ def quantize_append(latent, rope, slot_mapping, kv_cache):
 
     latent: bf16 or fp16 [N, >=512] (rows 16-byte aligned), rope: the same
     dtype [N, >=64], slot_mapping: int64 [N], kv_cache: uint8 [num_blocks,
-    block_size, 352].
+    block_size, 352 or 432].  The 432-byte record takes bf16 only.
     """
     n = latent.shape[0]
     if latent.dtype not in (torch.bfloat16, torch.float16) or rope.dtype != latent.dtype:
@@ -141,7 +164,12 @@ def quantize_append(latent, rope, slot_mapping, kv_cache):
     if latent.stride(-1) != 1 or rope.stride(-1) != 1 or not slot_mapping.is_contiguous():
         raise ValueError("inner dimensions must be contiguous")
     nb, bs, stride = _cache_geometry(kv_cache)
-    fn = "nvfp4_mla_quantize_append" + ("_fp16" if latent.dtype == torch.float16 else "")
+    if _ds(kv_cache):
+        if latent.dtype != torch.bfloat16:
+            raise ValueError("the 432-byte record stores bf16 RoPE: inputs must be bfloat16")
+        fn = "nvfp4_mla_quantize_append_ds_mla"
+    else:
+        fn = "nvfp4_mla_quantize_append" + ("_fp16" if latent.dtype == torch.float16 else "")
     code = getattr(lib(), fn)(
         _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(slot_mapping), n,
         _ptr(kv_cache), nb, bs, stride, _stream(kv_cache.device))
@@ -157,9 +185,10 @@ def dequantize_gather(kv_cache, slots, out=None):
     if out is None:
         out = torch.empty((n, QK_DIM), dtype=torch.bfloat16, device=kv_cache.device)
     nb, bs, stride = _cache_geometry(kv_cache)
-    code = lib().nvfp4_mla_dequantize_gather(_ptr(kv_cache), nb, bs, stride, _ptr(slots), n,
-                                             _ptr(out), _stream(kv_cache.device))
-    _check("nvfp4_mla_dequantize_gather", code)
+    fn = "nvfp4_mla_dequantize_gather" + _ds(kv_cache)
+    code = getattr(lib(), fn)(_ptr(kv_cache), nb, bs, stride, _ptr(slots), n,
+                              _ptr(out), _stream(kv_cache.device))
+    _check(fn, code)
     return out
 
 
@@ -204,11 +233,12 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
     if lse is None:
         lse = torch.empty((b, s, h), dtype=torch.float32, device=q.device)
     nb, bs, stride = _cache_geometry(kv_cache)
-    code = lib().nvfp4_mla_sparse_decode(
+    fn = "nvfp4_mla_sparse_decode" + _ds(kv_cache)
+    code = getattr(lib(), fn)(
         _ptr(q), _ptr(kv_cache), nb, bs, stride, _ptr(indices), b, s, h, topk, _ptr(sink),
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
-    _check("nvfp4_mla_sparse_decode", code)
+    _check(fn, code)
     return out, lse
 
 
@@ -243,12 +273,15 @@ def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, soft
         lse = torch.empty((b, s, h), dtype=torch.float32, device=q.device)
     nb0, bs0, st0 = _cache_geometry(kv_cache)
     nb1, bs1, st1 = _cache_geometry(extra_kv_cache)
-    code = lib().nvfp4_mla_sparse_decode_dual(
+    if kv_cache.shape[2] != extra_kv_cache.shape[2]:
+        raise ValueError("both caches must hold the same record (352 or 432 bytes)")
+    fn = "nvfp4_mla_sparse_decode_dual" + _ds(kv_cache)
+    code = getattr(lib(), fn)(
         _ptr(q), _ptr(kv_cache), nb0, bs0, st0, _ptr(indices) if topk0 else None, topk0,
         _ptr(extra_kv_cache), nb1, bs1, st1, _ptr(extra_indices) if topk1 else None, topk1,
         b, s, h, _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
-    _check("nvfp4_mla_sparse_decode_dual", code)
+    _check(fn, code)
     return out, lse
 
 

@@ -80,7 +80,8 @@ int check_device(int* cus) {
 }
 
 int check_cache(const void* kv_cache, int64_t num_blocks, int32_t block_size,
-                int64_t block_stride_bytes, int64_t* num_slots) {
+                int64_t block_stride_bytes, int64_t* num_slots,
+                int32_t record_bytes = NVFP4_MLA_RECORD_BYTES) {
   if (kv_cache == nullptr) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "kv_cache is NULL");
   if (!aligned(kv_cache, 16))
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "kv_cache must be 16-byte aligned");
@@ -88,10 +89,11 @@ int check_cache(const void* kv_cache, int64_t num_blocks, int32_t block_size,
   if (block_size < 1) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "block_size must be >= 1");
   if (block_stride_bytes % 16 != 0)
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "block_stride_bytes must be a multiple of 16");
-  if (block_stride_bytes < (int64_t)block_size * NVFP4_MLA_RECORD_BYTES)
+  if (block_stride_bytes < (int64_t)block_size * record_bytes)
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
-                "block_stride_bytes %lld < block_size * 352 = %lld",
-                (long long)block_stride_bytes, (long long)block_size * NVFP4_MLA_RECORD_BYTES);
+                "block_stride_bytes %lld < block_size * %d = %lld",
+                (long long)block_stride_bytes, record_bytes,
+                (long long)block_size * record_bytes);
   const int64_t slots = num_blocks * (int64_t)block_size;
   if (num_blocks > INT64_C(0x7FFFFFFF) || slots > INT64_C(0x7FFFFFFF))
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
@@ -101,8 +103,10 @@ int check_cache(const void* kv_cache, int64_t num_blocks, int32_t block_size,
   return NVFP4_MLA_OK;
 }
 
-nvfp4::PageAddr make_page_addr(int32_t block_size, int64_t block_stride_bytes) {
+nvfp4::PageAddr make_page_addr(int32_t block_size, int64_t block_stride_bytes,
+                               int32_t record_bytes = NVFP4_MLA_RECORD_BYTES) {
   nvfp4::PageAddr pa{};
+  pa.record_bytes = (uint32_t)record_bytes;
   pa.block_stride = (uint64_t)block_stride_bytes;
   pa.block_size = (uint32_t)block_size;
   pa.pow2 = (block_size & (block_size - 1)) == 0;
@@ -186,10 +190,11 @@ int quantize_append_impl(const char* fn, const void* latent_bf16, int64_t latent
                          const void* rope_bf16, int64_t rope_row_stride,
                          const int64_t* slot_mapping, int64_t num_tokens, uint8_t* kv_cache,
                          int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
-                         bool f16_input, void* stream) {
+                         bool f16_input, int32_t record_bytes, void* stream) {
   if (num_tokens < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
   int64_t num_slots = 0;
-  int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots,
+                       record_bytes);
   if (rc) return rc;
   if (num_tokens > 0) {
     if (!latent_bf16 || !rope_bf16 || !slot_mapping)
@@ -211,7 +216,7 @@ int quantize_append_impl(const char* fn, const void* latent_bf16, int64_t latent
   hipError_t e = nvfp4::launch_quantize_append(
       static_cast<const uint16_t*>(latent_bf16), latent_row_stride,
       static_cast<const uint16_t*>(rope_bf16), rope_row_stride, slot_mapping, num_tokens, kv_cache,
-      num_slots, make_page_addr(block_size, block_stride_bytes), f16_input,
+      num_slots, make_page_addr(block_size, block_stride_bytes, record_bytes), f16_input,
       static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
@@ -235,7 +240,8 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
                        const int32_t* indices, int32_t topk0, const ExtraCache* extra,
                        int32_t batch, int32_t s_q, int32_t h_q, const float* attn_sink,
                        float softmax_scale, void* out_bf16, float* lse, void* workspace,
-                       size_t workspace_bytes_in, int32_t num_splits, void* stream) {
+                       size_t workspace_bytes_in, int32_t num_splits, int32_t record_bytes,
+                       void* stream) {
   if (extra && (topk0 < 0 || extra->topk < 0 || topk0 > 65536 || extra->topk > 65536))
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d and extra_topk = %d must be >= 0",
                 topk0, extra ? extra->topk : 0);
@@ -243,11 +249,11 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   int rc = check_decode_shape(batch, s_q, h_q, topk);
   if (rc) return rc;
   int64_t num_slots = 0, num_slots1 = 0;
-  rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots, record_bytes);
   if (rc) return rc;
   if (extra) {
     rc = check_cache(extra->kv_cache, extra->num_blocks, extra->block_size,
-                     extra->block_stride_bytes, &num_slots1);
+                     extra->block_stride_bytes, &num_slots1, record_bytes);
     if (rc) return fail(rc, "extra cache: %s", g_last_error.c_str());
   }
   if (num_splits < 0 || num_splits > NVFP4_MLA_MAX_SPLITS)
@@ -286,13 +292,13 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   nvfp4::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q_bf16);
   a.cache = kv_cache;
-  a.pa = make_page_addr(block_size, block_stride_bytes);
+  a.pa = make_page_addr(block_size, block_stride_bytes, record_bytes);
   a.num_slots = num_slots;
   a.indices = indices;
   a.topk0 = topk0;
   if (extra) {
     a.cache1 = extra->kv_cache;
-    a.pa1 = make_page_addr(extra->block_size, extra->block_stride_bytes);
+    a.pa1 = make_page_addr(extra->block_size, extra->block_stride_bytes, record_bytes);
     a.num_slots1 = num_slots1;
     a.indices1 = extra->indices;
   }
@@ -317,52 +323,13 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-int nvfp4_mla_abi_version(void) { return NVFP4_MLA_ABI_VERSION; }
-
-const char* nvfp4_mla_last_error(void) { return g_last_error.c_str(); }
-
-int nvfp4_mla_check_format(int32_t record_bytes, int32_t nope_dim, int32_t rope_dim,
-                           int32_t v_dim) {
-  if (record_bytes != NVFP4_MLA_RECORD_BYTES || nope_dim != NVFP4_MLA_NOPE_DIM ||
-      rope_dim != NVFP4_MLA_ROPE_DIM || v_dim != NVFP4_MLA_V_DIM)
-    return fail(NVFP4_MLA_ERR_UNSUPPORTED_FORMAT,
-                "unsupported format: record %d B, NoPE %d, RoPE %d, d_v %d (this library "
-                "implements the 352 B NVFP4 record with 512/64/512)",
-                record_bytes, nope_dim, rope_dim, v_dim);
-  return ok();
-}
-
-
-int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride,
-                              const void* rope_bf16, int64_t rope_row_stride,
-                              const int64_t* slot_mapping, int64_t num_tokens,
-                              uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                              int64_t block_stride_bytes, void* stream) {
-  return quantize_append_impl("quantize_append", latent_bf16, latent_row_stride, rope_bf16,
-                              rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
-                              block_size, block_stride_bytes, false, stream);
-}
-
-int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_stride,
-                                   const void* rope_fp16, int64_t rope_row_stride,
-                                   const int64_t* slot_mapping, int64_t num_tokens,
-                                   uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                                   int64_t block_stride_bytes, void* stream) {
-  return quantize_append_impl("quantize_append_fp16", latent_fp16, latent_row_stride, rope_fp16,
-                              rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
-                              block_size, block_stride_bytes, true, stream);
-}
-
-int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                                int64_t block_stride_bytes, const int32_t* slots, int64_t n,
-                                void* out_bf16, void* stream) {
+int dequantize_gather_impl(const char* fn, const uint8_t* kv_cache, int64_t num_blocks,
+                           int32_t block_size, int64_t block_stride_bytes, const int32_t* slots,
+                           int64_t n, void* out_bf16, int32_t record_bytes, void* stream) {
   if (n < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "n must be >= 0");
   int64_t num_slots = 0;
-  int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots);
+  int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots,
+                       record_bytes);
   if (rc) return rc;
   if (n > 0) {
     if (!slots || !out_bf16)
@@ -375,12 +342,83 @@ int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int
   rc = check_device(nullptr);
   if (rc) return rc;
   hipError_t e = nvfp4::launch_dequantize_gather(kv_cache, num_slots,
-                                                 make_page_addr(block_size, block_stride_bytes),
+                                                 make_page_addr(block_size, block_stride_bytes,
+                                                                record_bytes),
                                                  slots, n, static_cast<uint16_t*>(out_bf16),
                                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
-    return fail(NVFP4_MLA_ERR_HIP, "dequantize_gather launch failed: %s", hipGetErrorString(e));
+    return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_mla_abi_version(void) { return NVFP4_MLA_ABI_VERSION; }
+
+const char* nvfp4_mla_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_mla_check_format(int32_t record_bytes, int32_t nope_dim, int32_t rope_dim,
+                           int32_t v_dim) {
+  if ((record_bytes != NVFP4_MLA_RECORD_BYTES && record_bytes != NVFP4_MLA_DS_MLA_RECORD_BYTES) ||
+      nope_dim != NVFP4_MLA_NOPE_DIM || rope_dim != NVFP4_MLA_ROPE_DIM || v_dim != NVFP4_MLA_V_DIM)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_FORMAT,
+                "unsupported format: record %d B, NoPE %d, RoPE %d, d_v %d (this library "
+                "implements the 352 B and 432 B NVFP4 records with 512/64/512)",
+                record_bytes, nope_dim, rope_dim, v_dim);
+  return ok();
+}
+
+
+int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride,
+                              const void* rope_bf16, int64_t rope_row_stride,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                              int64_t block_stride_bytes, void* stream) {
+  return quantize_append_impl("quantize_append", latent_bf16, latent_row_stride, rope_bf16,
+                              rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
+                              block_size, block_stride_bytes, false, NVFP4_MLA_RECORD_BYTES,
+                              stream);
+}
+
+int nvfp4_mla_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row_stride,
+                                     const void* rope_bf16, int64_t rope_row_stride,
+                                     const int64_t* slot_mapping, int64_t num_tokens,
+                                     uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                                     int64_t block_stride_bytes, void* stream) {
+  return quantize_append_impl("quantize_append_ds_mla", latent_bf16, latent_row_stride,
+                              rope_bf16, rope_row_stride, slot_mapping, num_tokens, kv_cache,
+                              num_blocks, block_size, block_stride_bytes, false,
+                              NVFP4_MLA_DS_MLA_RECORD_BYTES, stream);
+}
+
+int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_stride,
+                                   const void* rope_fp16, int64_t rope_row_stride,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                                   int64_t block_stride_bytes, void* stream) {
+  return quantize_append_impl("quantize_append_fp16", latent_fp16, latent_row_stride, rope_fp16,
+                              rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
+                              block_size, block_stride_bytes, true, NVFP4_MLA_RECORD_BYTES,
+                              stream);
+}
+
+int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                                int64_t block_stride_bytes, const int32_t* slots, int64_t n,
+                                void* out_bf16, void* stream) {
+  return dequantize_gather_impl("dequantize_gather", kv_cache, num_blocks, block_size,
+                                block_stride_bytes, slots, n, out_bf16, NVFP4_MLA_RECORD_BYTES,
+                                stream);
+}
+
+int nvfp4_mla_dequantize_gather_ds_mla(const uint8_t* kv_cache, int64_t num_blocks,
+                                       int32_t block_size, int64_t block_stride_bytes,
+                                       const int32_t* slots, int64_t n, void* out_bf16,
+                                       void* stream) {
+  return dequantize_gather_impl("dequantize_gather_ds_mla", kv_cache, num_blocks, block_size,
+                                block_stride_bytes, slots, n, out_bf16,
+                                NVFP4_MLA_DS_MLA_RECORD_BYTES, stream);
 }
 
 int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
@@ -422,7 +460,21 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache, int64_t
   return sparse_decode_impl("sparse_decode", q_bf16, kv_cache, num_blocks, block_size,
                             block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
                             attn_sink, softmax_scale, out_bf16, lse, workspace,
-                            workspace_bytes_in, num_splits, stream);
+                            workspace_bytes_in, num_splits, NVFP4_MLA_RECORD_BYTES, stream);
+}
+
+int nvfp4_mla_sparse_decode_ds_mla(const void* q_bf16, const uint8_t* kv_cache,
+                                   int64_t num_blocks, int32_t block_size,
+                                   int64_t block_stride_bytes, const int32_t* indices,
+                                   int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
+                                   const float* attn_sink, float softmax_scale, void* out_bf16,
+                                   float* lse, void* workspace, size_t workspace_bytes_in,
+                                   int32_t num_splits, void* stream) {
+  return sparse_decode_impl("sparse_decode_ds_mla", q_bf16, kv_cache, num_blocks, block_size,
+                            block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
+                            attn_sink, softmax_scale, out_bf16, lse, workspace,
+                            workspace_bytes_in, num_splits, NVFP4_MLA_DS_MLA_RECORD_BYTES,
+                            stream);
 }
 
 int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache, int64_t num_blocks,
@@ -440,7 +492,24 @@ int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache, in
   return sparse_decode_impl("sparse_decode_dual", q_bf16, kv_cache, num_blocks, block_size,
                             block_stride_bytes, indices, topk, &extra, batch, s_q, h_q,
                             attn_sink, softmax_scale, out_bf16, lse, workspace,
-                            workspace_bytes_in, num_splits, stream);
+                            workspace_bytes_in, num_splits, NVFP4_MLA_RECORD_BYTES, stream);
+}
+
+int nvfp4_mla_sparse_decode_dual_ds_mla(
+    const void* q_bf16, const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+    int64_t block_stride_bytes, const int32_t* indices, int32_t topk,
+    const uint8_t* extra_kv_cache, int64_t extra_num_blocks, int32_t extra_block_size,
+    int64_t extra_block_stride_bytes, const int32_t* extra_indices, int32_t extra_topk,
+    int32_t batch, int32_t s_q, int32_t h_q, const float* attn_sink, float softmax_scale,
+    void* out_bf16, float* lse, void* workspace, size_t workspace_bytes_in, int32_t num_splits,
+    void* stream) {
+  const ExtraCache extra{extra_kv_cache, extra_num_blocks, extra_block_size,
+                         extra_block_stride_bytes, extra_indices, extra_topk};
+  return sparse_decode_impl("sparse_decode_dual_ds_mla", q_bf16, kv_cache, num_blocks,
+                            block_size, block_stride_bytes, indices, topk, &extra, batch, s_q,
+                            h_q, attn_sink, softmax_scale, out_bf16, lse, workspace,
+                            workspace_bytes_in, num_splits, NVFP4_MLA_DS_MLA_RECORD_BYTES,
+                            stream);
 }
 
 int nvfp4_mla_combine(const float* o_partial, const float* lse_partial, int32_t num_splits,

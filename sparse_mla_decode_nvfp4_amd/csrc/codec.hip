@@ -1,13 +1,15 @@
-// Quantize-append (write path) and dequantize-gather kernels for the 352-byte
-// NVFP4 record.  gfx950.
+// Quantize-append (write path) and dequantize-gather kernels for the 352- and
+// 432-byte NVFP4 records.  gfx950.
 //
 // Write rule (vLLM PR #82 "kv: nvfp4_ds_mla -- 4-bit NVFP4 KV cache for B12X
-// sparse MLA (SM120)", Fix and Tests; layout from FlashMLA PR #18, PR
-// description): per 16-element NoPE block, scale S = E4M3(amax/6) rounded to
-// nearest-even and saturated at 448; each element's magnitude is rounded to
-// the nearest E2M1 grid point of |x|/value(S) (ties to the even code, 0 when
-// the scale is 0), its sign copied; RoPE is stored as unscaled E4M3 (RNE,
-// saturating, sign kept).  Tokens whose slot is negative are skipped.
+// sparse MLA (SM120)", Fix and Tests; 352-byte layout from FlashMLA PR #18,
+// PR description): per 16-element NoPE block, scale S = E4M3(amax/6) rounded
+// to nearest-even and saturated at 448; each element's magnitude is rounded
+// to the nearest E2M1 grid point of |x|/value(S) (ties to the even code, 0
+// when the scale is 0), its sign copied.  The 352-byte record stores RoPE as
+// unscaled E4M3 (RNE, saturating, sign kept); the 432-byte record copies the
+// bf16 RoPE bits verbatim and zeroes its 16-byte pad.  Tokens whose slot is
+// negative are skipped.
 #include "device_common.h"
 #include "launch.h"
 
@@ -43,16 +45,17 @@ __device__ __forceinline__ float widen16(uint32_t bits16) {
 
 // One wavefront per token; 4 tokens per 256-thread block.  Lane l quantizes
 // NoPE elements [8l, 8l+8) (block l/2) and RoPE element l; the record is
-// assembled in LDS and written with 22 16-byte stores.  The input is bf16, or
-// fp16 when kF16: every fp16 or bf16 value is exact in fp32, so the rounding
-// below is the same for both.
-template <bool kF16>
+// assembled in LDS and written with 16-byte stores (22 or 27).  The input is
+// bf16, or fp16 when kF16 (352-byte record only): every fp16 or bf16 value is
+// exact in fp32, so the rounding below is the same for both.
+template <bool kF16, class F>
 __global__ void __launch_bounds__(256)
 quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
                        const uint16_t* __restrict__ rope, int64_t rstride,
                        const int64_t* __restrict__ slot_mapping, int64_t num_tokens,
                        uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa) {
-  __shared__ __attribute__((aligned(16))) uint8_t rec[4][kRecordBytes];
+  static_assert(!(kF16 && F::kBf16Rope), "the 432-byte record holds bf16 RoPE");
+  __shared__ __attribute__((aligned(16))) uint8_t rec[4][F::kBytes];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
@@ -82,21 +85,29 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
     packed |= code << (4 * i);
   }
   reinterpret_cast<uint32_t*>(r)[lane] = packed;
-  if ((lane & 1) == 0) r[kScaleOffset + scale_byte(lane >> 1)] = (uint8_t)scode;
+  if ((lane & 1) == 0) r[F::scale_at(lane >> 1)] = (uint8_t)scode;
   // ---- RoPE: lane l handles element l
-  const float rv = widen16<kF16>((uint32_t)rope[tok * rstride + lane]);
-  const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
-  r[kRopeOffset + lane] = (uint8_t)rcode;
+  const uint32_t rbits = (uint32_t)rope[tok * rstride + lane];
+  if constexpr (F::kBf16Rope) {
+    reinterpret_cast<uint16_t*>(r + F::kRopeOff)[lane] = (uint16_t)rbits;   // verbatim
+    if (lane < 4) reinterpret_cast<uint32_t*>(r + F::kPadOff)[lane] = 0u;
+  } else {
+    const float rv = widen16<kF16>(rbits);
+    const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
+    r[F::kRopeOff + lane] = (uint8_t)rcode;
+  }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  if (lane < kRecordBytes / 16) {
+  if (lane < F::kBytes / 16) {
     uint8_t* dst = cache + pa.offset((uint32_t)slot);
     reinterpret_cast<u32x4*>(dst)[lane] = reinterpret_cast<const u32x4*>(r)[lane];
   }
 }
 
 // One wavefront per output row: lane l dequantizes NoPE elements [8l, 8l+8)
-// through the decode's own routine; lanes 0..7 produce the 64 RoPE values.
+// through the decode's own routine; lanes 0..7 produce the 64 RoPE values
+// (E4M3 -> bf16, exact, or the stored bf16 bits).
+template <class F>
 __global__ void __launch_bounds__(256)
 dequantize_gather_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa,
                          const int32_t* __restrict__ slots, int64_t n,
@@ -116,16 +127,20 @@ dequantize_gather_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, P
   const uint8_t* src = cache + pa.offset((uint32_t)slot);
   const uint32_t nib = reinterpret_cast<const uint32_t*>(src)[lane];
   const int s = lane >> 1;
-  const float sv = e4m3x2_to_f32<0>((uint32_t)src[kScaleOffset + scale_byte(s)]).x;
+  const float sv = e4m3x2_to_f32<0>((uint32_t)src[F::scale_at(s)]).x;
   uint32_t o[4];
   dequant8(nib, sv, o);
   const u32x4 ov = {o[0], o[1], o[2], o[3]};
   dst[lane] = ov;
   if (lane < 8) {
-    const u32x2 rb = reinterpret_cast<const u32x2*>(src + kRopeOffset)[lane];
-    const u32x4 rv = {e4m3x2_to_bf16x2<0>(rb.x), e4m3x2_to_bf16x2<1>(rb.x),
-                      e4m3x2_to_bf16x2<0>(rb.y), e4m3x2_to_bf16x2<1>(rb.y)};
-    dst[64 + lane] = rv;
+    if constexpr (F::kBf16Rope) {
+      dst[64 + lane] = reinterpret_cast<const u32x4*>(src + F::kRopeOff)[lane];
+    } else {
+      const u32x2 rb = reinterpret_cast<const u32x2*>(src + F::kRopeOff)[lane];
+      const u32x4 rv = {e4m3x2_to_bf16x2<0>(rb.x), e4m3x2_to_bf16x2<1>(rb.x),
+                        e4m3x2_to_bf16x2<0>(rb.y), e4m3x2_to_bf16x2<1>(rb.y)};
+      dst[64 + lane] = rv;
+    }
   }
 }
 
@@ -135,15 +150,21 @@ hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
                                   uint8_t* cache, int64_t num_slots, const PageAddr& pa,
                                   bool f16_input, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int64_t blocks = (num_tokens + 3) / 4;
-  if (f16_input)
-    hipLaunchKernelGGL(quantize_append_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+  const dim3 grid((uint32_t)((num_tokens + 3) / 4));
+  if (pa.record_bytes == Fmt432::kBytes) {
+    if (f16_input) return hipErrorInvalidValue;    // rejected by the caller already
+    hipLaunchKernelGGL((quantize_append_kernel<false, Fmt432>), grid, dim3(256), 0, stream,
                        latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
                        num_slots, pa);
-  else
-    hipLaunchKernelGGL(quantize_append_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+  } else if (f16_input) {
+    hipLaunchKernelGGL((quantize_append_kernel<true, Fmt352>), grid, dim3(256), 0, stream,
                        latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
                        num_slots, pa);
+  } else {
+    hipLaunchKernelGGL((quantize_append_kernel<false, Fmt352>), grid, dim3(256), 0, stream,
+                       latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
+                       num_slots, pa);
+  }
   return hipGetLastError();
 }
 
@@ -151,9 +172,13 @@ hipError_t launch_dequantize_gather(const uint8_t* cache, int64_t num_slots, con
                                     const int32_t* slots, int64_t n, uint16_t* out,
                                     hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int64_t blocks = (n + 3) / 4;
-  hipLaunchKernelGGL(dequantize_gather_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     cache, num_slots, pa, slots, n, out);
+  const dim3 grid((uint32_t)((n + 3) / 4));
+  if (pa.record_bytes == Fmt432::kBytes)
+    hipLaunchKernelGGL(dequantize_gather_kernel<Fmt432>, grid, dim3(256), 0, stream,
+                       cache, num_slots, pa, slots, n, out);
+  else
+    hipLaunchKernelGGL(dequantize_gather_kernel<Fmt352>, grid, dim3(256), 0, stream,
+                       cache, num_slots, pa, slots, n, out);
   return hipGetLastError();
 }
 

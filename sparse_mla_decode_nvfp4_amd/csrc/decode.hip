@@ -86,22 +86,43 @@ __device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, h16x2));
 }
 
-struct RawTok {          // the bytes one lane needs of one token record
-  u32x2 nope[8];         // NoPE blocks 4c+g, c = 0..7
-  u32x2 scale;           // scale bytes 8g .. 8g+7 (= blocks 4c+g)
-  u32x4 rope;            // RoPE elements 16g .. 16g+15
+// The bytes one lane needs of one token record.  Lane group g takes eight
+// NoPE blocks whose scales are eight consecutive scale bytes: blocks 4c+g
+// (c = 0..7) in the 352-byte record, whose scale area is permuted, and blocks
+// 8g+c in the 432-byte record, whose scales are in block order.
+template <class F>
+struct RawTok {
+  u32x2 nope[8];         // NoPE block blk(g, c), c = 0..7
+  u32x2 scale;           // scale bytes 8g .. 8g+7 (= blocks blk(g, c))
+  u32x4 rope;            // RoPE elements 16g .. 16g+15 (E4M3)
 };
+template <>
+struct RawTok<Fmt432> {
+  u32x2 nope[8];
+  u32x2 scale;
+  u32x4 rope[2];         // RoPE elements 16g .. 16g+15 (bf16)
+};
+
+// NoPE block of lane group g's c-th k-step pair.
+template <class F>
+__device__ __forceinline__ int blk(int g, int c) { return F::kBf16Rope ? 8 * g + c : 4 * c + g; }
 
 // Unconditional loads (uniform control flow keeps the prefetch in flight:
 // after a divergent load the compiler can only wait for every outstanding
 // load).  Invalid tokens read record 0, which always exists; their scale
 // bytes are zeroed when consumed, so their NoPE values are exact zeros and
 // cannot carry NaN into P V, and their scores are masked.
-__device__ __forceinline__ void load_tok(RawTok& t, const uint8_t* rec, int g) {
+template <class F>
+__device__ __forceinline__ void load_tok(RawTok<F>& t, const uint8_t* rec, int g) {
 #pragma unroll
-  for (int c = 0; c < 8; c++) t.nope[c] = *reinterpret_cast<const u32x2*>(rec + 32 * c + 8 * g);
-  t.scale = *reinterpret_cast<const u32x2*>(rec + kScaleOffset + 8 * g);
-  t.rope = *reinterpret_cast<const u32x4*>(rec + kRopeOffset + 16 * g);
+  for (int c = 0; c < 8; c++) t.nope[c] = *reinterpret_cast<const u32x2*>(rec + 8 * blk<F>(g, c));
+  t.scale = *reinterpret_cast<const u32x2*>(rec + F::kScaleOff + 8 * g);
+  if constexpr (F::kBf16Rope) {
+    t.rope[0] = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 32 * g);
+    t.rope[1] = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 32 * g + 16);
+  } else {
+    t.rope = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 16 * g);
+  }
 }
 
 
@@ -139,7 +160,7 @@ __device__ __forceinline__ h16x8 rope8_f16(uint32_t x, uint32_t y) {
 //   ks 16, 17 cover RoPE dims 16g + 8*(ks-16) + [0,8).  Q is laid out to match.
 //   PV (16x16x32): A = P[head n][token 32ks+8g+i], B = V[token 32ks+8g+i][dv],
 //   C = O[head 4g+r][dv 128w + 16nb + n].
-template <bool kDual>
+template <bool kDual, class F>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 decode_tile16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * kVChunk];
@@ -182,7 +203,7 @@ decode_tile16_kernel(DecodeArgs a) {
   const RecRef r0 = resolve(load_idx(tile), tile);
   bool ok_cur = r0.ok;             // this lane's token of the current tile takes part
   int32_t idx_nxt = load_idx(tile + 1);
-  RawTok cur;
+  RawTok<F> cur;
   load_tok(cur, r0.ptr, g);
 
   // ---- Q^T operand registers (head n, k-chunk g) in fp16 with a per-head
@@ -195,7 +216,7 @@ decode_tile16_kernel(DecodeArgs a) {
     u32x4 raw[18];
 #pragma unroll
     for (int ks = 0; ks < 16; ks++)
-      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * (4 * (ks >> 1) + g) + 8 * (ks & 1));
+      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * blk<F>(g, ks >> 1) + 8 * (ks & 1));
 #pragma unroll
     for (int ks = 16; ks < 18; ks++)
       raw[ks] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
@@ -216,13 +237,27 @@ decode_tile16_kernel(DecodeArgs a) {
     const float mul = a.scale_log2 < 0.f ? -__builtin_ldexpf(1.0f, -p) : __builtin_ldexpf(1.0f, -p);
     qscale = fabsf(a.scale_log2) * __builtin_ldexpf(1.0f, p);
 #pragma unroll
-    for (int ks = 0; ks < 18; ks++)
+    for (int ks = 0; ks < 18; ks++) {
+      if (F::kBf16Rope && ks >= 16) {
+        // bf16 RoPE keys meet a bf16 Q operand (x * 2^-p is exact in bf16),
+        // held in the same registers
+        bf16x8 v;
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const uint32_t x = raw[ks][w];
-        qB[ks][2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
-        qB[ks][2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+        for (int w = 0; w < 4; w++) {
+          const uint32_t x = raw[ks][w];
+          v[2 * w] = (__bf16)(__uint_as_float(x << 16) * mul);
+          v[2 * w + 1] = (__bf16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+        }
+        qB[ks] = __builtin_bit_cast(h16x8, v);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const uint32_t x = raw[ks][w];
+          qB[ks][2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
+          qB[ks][2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+        }
       }
+    }
   }
 
   f32x4 acc_o[8];
@@ -234,17 +269,19 @@ decode_tile16_kernel(DecodeArgs a) {
   float m_r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float l_part = 0.f;          // this lane's share of head n's denominator
 
-  // V tile addresses.  Write (k-step 2c+h): chunk 8c + 2g + h, token
-  // my_tok.  Read (PV k-step ks, half hb, block nb): token 32ks + 8g + 4hb +
-  // (l%16)/4, chunk 16w + 2nb + ((l%4)>>1), byte 8(l&1).
-  const uint32_t vw_base = (uint32_t)(size_t)(vtile + 2 * g * kVChunk + my_tok * 16);
+  // V tile addresses.  Write (k-step 2c+h): chunk 2 blk(g, c) + h (= 8c + 2g
+  // + h, or 16g + 2c + h), token my_tok.  Read (PV k-step ks, half hb, block
+  // nb): token 32ks + 8g + 4hb + (l%16)/4, chunk 16w + 2nb + ((l%4)>>1), byte
+  // 8(l&1).
+  constexpr int kVwStep = F::kBf16Rope ? 2 : 8;       // chunks between c and c+1
+  const uint32_t vw_base = (uint32_t)(size_t)(vtile + 2 * blk<F>(g, 0) * kVChunk + my_tok * 16);
   const uint32_t vr_base = (uint32_t)(size_t)(vtile + (16 * wave + ((lane & 3) >> 1)) * kVChunk +
                                              (8 * g + ((lane >> 2) & 3)) * 16 + 8 * (lane & 1));
 
   // One tile step.  `cur` holds this lane's bytes of tile t, `nxt` receives
   // tile t+1's; the loop below alternates the two buffers so the prefetched
   // bytes are never copied.
-  auto step = [&](RawTok& cur, RawTok& nxt, int t) {
+  auto step = [&](RawTok<F>& cur, RawTok<F>& nxt, int t) {
     // ---- prefetch: indices two tiles ahead, token bytes one tile ahead
     const int32_t idx_nn = load_idx(t + 2);
     const RecRef rn = resolve(idx_nxt, t + 1);
@@ -270,18 +307,25 @@ decode_tile16_kernel(DecodeArgs a) {
     f32x4 s_acc = {0.f, 0.f, 0.f, 0.f}, s_acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; c++) {
-      const h16x2 F = mantissa_f16(sc[c]);
+      const h16x2 Fm = mantissa_f16(sc[c]);
 #pragma unroll
       for (int h = 0; h < 2; h++) {
-        const h16x8 k = dequant8_f16(h ? cur.nope[c].y : cur.nope[c].x, sc[c], F);
+        const h16x8 k = dequant8_f16(h ? cur.nope[c].y : cur.nope[c].x, sc[c], Fm);
         *reinterpret_cast<__attribute__((address_space(3))) h16x8*>(
-            (lds_b*)(size_t)vw_base + (8 * c + h) * kVChunk) = k;
+            (lds_b*)(size_t)vw_base + (kVwStep * c + h) * kVChunk) = k;
         if (h == 0) s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c], s_acc, 0, 0, 0);
         else s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c + 1], s_acc1, 0, 0, 0);
       }
     }
-    s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rope8_f16(cur.rope.x, cur.rope.y), qB[16], s_acc, 0, 0, 0);
-    s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(rope8_f16(cur.rope.z, cur.rope.w), qB[17], s_acc1, 0, 0, 0);
+    if constexpr (F::kBf16Rope) {
+      s_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.rope[0]),
+                                                     __builtin_bit_cast(bf16x8, qB[16]), s_acc, 0, 0, 0);
+      s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.rope[1]),
+                                                      __builtin_bit_cast(bf16x8, qB[17]), s_acc1, 0, 0, 0);
+    } else {
+      s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rope8_f16(cur.rope.x, cur.rope.y), qB[16], s_acc, 0, 0, 0);
+      s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(rope8_f16(cur.rope.z, cur.rope.w), qB[17], s_acc1, 0, 0, 0);
+    }
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; r++)
@@ -347,7 +391,7 @@ decode_tile16_kernel(DecodeArgs a) {
     idx_nxt = idx_nn;
   };
 
-  RawTok other;
+  RawTok<F> other;
   for (; tile + 1 < tile1; tile += 2) {
     step(cur, other, tile);
     step(other, cur, tile + 1);
@@ -427,10 +471,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   if (decode_uses_w32(a.h_q)) return launch_decode_w32(a, stream);
   const int grid = a.rows * (a.h_q / 16) * a.splits;
-  if (a.cache1)
-    hipLaunchKernelGGL(decode_tile16_kernel<true>, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  const bool f432 = a.pa.record_bytes == Fmt432::kBytes;
+  if (a.cache1 && f432)
+    hipLaunchKernelGGL((decode_tile16_kernel<true, Fmt432>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else if (a.cache1)
+    hipLaunchKernelGGL((decode_tile16_kernel<true, Fmt352>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else if (f432)
+    hipLaunchKernelGGL((decode_tile16_kernel<false, Fmt432>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_tile16_kernel<false>, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((decode_tile16_kernel<false, Fmt352>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

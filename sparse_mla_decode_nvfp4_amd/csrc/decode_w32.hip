@@ -48,6 +48,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) float lds_f32;
@@ -75,21 +76,40 @@ static_assert(32 * 4096 <= kOffStat, "merge slots overlap the statistics");
 
 // This lane's share of one record (token n of the chunk, half hf, lane group
 // g): NoPE blocks s = 16hf + 4g + u (u = 0..3), 32 contiguous bytes; their
-// scales, byte g of the dword at 320 + 8u + 4hf (block s's scale sits at
-// 320 + 8(s&3) + (s>>2)); RoPE dims 32hf + 8g .. +7.
-struct RawP {
+// scales; RoPE dims 32hf + 8g .. +7.  In the 352-byte record block s's scale
+// sits at 320 + 8(s&3) + (s>>2), so the four are byte g of the dwords at
+// 320 + 8u + 4hf, and RoPE is 8 E4M3 bytes; in the 432-byte record they are
+// the four bytes of the dword at 256 + 16hf + 4g, and RoPE is 8 bf16.
+template <class F>
+struct RawP;
+template <>
+struct RawP<Fmt352> {
   u32x4 nope[2];
   uint32_t sc[4];
   u32x2 rope;
+  __device__ __forceinline__ uint32_t scale(int u, int g) const { return (sc[u] >> (8 * g)) & 0xFFu; }
+};
+template <>
+struct RawP<Fmt432> {
+  u32x4 nope[2];
+  uint32_t sc;
+  u32x4 rope;
+  __device__ __forceinline__ uint32_t scale(int u, int) const { return (sc >> (8 * u)) & 0xFFu; }
 };
 
-__device__ __forceinline__ void load_nope(RawP& r, int q, const uint8_t* rec, int hf, int g) {
+template <class F>
+__device__ __forceinline__ void load_nope(RawP<F>& r, int q, const uint8_t* rec, int hf, int g) {
   r.nope[q] = *reinterpret_cast<const u32x4*>(rec + 128 * hf + 32 * g + 16 * q);
 }
-__device__ __forceinline__ void load_tail(RawP& r, const uint8_t* rec, int hf, int g) {
+__device__ __forceinline__ void load_tail(RawP<Fmt352>& r, const uint8_t* rec, int hf, int g) {
 #pragma unroll
-  for (int u = 0; u < 4; u++) r.sc[u] = *reinterpret_cast<const uint32_t*>(rec + kScaleOffset + 8 * u + 4 * hf);
-  r.rope = *reinterpret_cast<const u32x2*>(rec + kRopeOffset + 32 * hf + 8 * g);
+  for (int u = 0; u < 4; u++)
+    r.sc[u] = *reinterpret_cast<const uint32_t*>(rec + Fmt352::kScaleOff + 8 * u + 4 * hf);
+  r.rope = *reinterpret_cast<const u32x2*>(rec + Fmt352::kRopeOff + 32 * hf + 8 * g);
+}
+__device__ __forceinline__ void load_tail(RawP<Fmt432>& r, const uint8_t* rec, int hf, int g) {
+  r.sc = *reinterpret_cast<const uint32_t*>(rec + Fmt432::kScaleOff + 16 * hf + 4 * g);
+  r.rope = *reinterpret_cast<const u32x4*>(rec + Fmt432::kRopeOff + 64 * hf + 16 * g);
 }
 
 __device__ __forceinline__ void lds_sync_p() {
@@ -155,7 +175,7 @@ struct IntC {
 //   C = S^T[token 4g+r][head 16b+n] for head blocks b = 0, 1.
 //   PV (32x32x16): A = P[head tl][token 8kg+i], B = V[token 8kg+i][dv 32nb +
 //   tl], C = O[head acc_row(r, kg)][dv 256hf + 32nb + tl].
-template <bool kDual>
+template <bool kDual, class F>
 __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_p[];
   lds_u8* const lds = (lds_u8*)smem_p;
@@ -221,7 +241,7 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 
   // the first chunk's indices and records are requested before the Q
   // set-up below, which hides part of their latency
-  RawP buf;
+  RawP<F> buf;
   bool ok_cur = false;
   int32_t idx_nxt = -1;
   if (my_n > 0) {
@@ -277,14 +297,27 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
       const float mul = a.scale_log2 < 0.f ? -__builtin_ldexpf(1.0f, -p) : __builtin_ldexpf(1.0f, -p);
 #pragma unroll
       for (int j = 0; j < 9; j++) {
-        f16x8 v;
+        lds_u8* const dst = qlds + (((hf * 2 + pr) * 9 + j) * 64 + lane) * 16;
+        if (F::kBf16Rope && j == 8) {
+          // bf16 RoPE keys meet a bf16 Q operand (x * 2^-p is exact in bf16)
+          bf16x8 v;
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
-          const uint32_t x = raw[j][w];
-          v[2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
-          v[2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+          for (int w = 0; w < 4; w++) {
+            const uint32_t x = raw[j][w];
+            v[2 * w] = (__bf16)(__uint_as_float(x << 16) * mul);
+            v[2 * w + 1] = (__bf16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+          }
+          *reinterpret_cast<lds_bf16x8*>(dst) = v;
+        } else {
+          f16x8 v;
+#pragma unroll
+          for (int w = 0; w < 4; w++) {
+            const uint32_t x = raw[j][w];
+            v[2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
+            v[2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+          }
+          *reinterpret_cast<lds_f16x8*>(dst) = v;
         }
-        *reinterpret_cast<lds_f16x8*>(qlds + (((hf * 2 + pr) * 9 + j) * 64 + lane) * 16) = v;
       }
     }
     lds_sync_p();
@@ -318,7 +351,7 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   // bytes (raw index nxt_raw, loaded a chunk earlier) right after its use.
   f32x4 sacc[2];
   uint32_t vm16 = 0;
-  auto pre = [&](RawP& cur, bool& cur_ok, int32_t& nxt_raw, int pos) {
+  auto pre = [&](RawP<F>& cur, bool& cur_ok, int32_t& nxt_raw, int pos) {
     const int32_t nxt2_raw = load_idx(pos + 2);
     const bool v = cur_ok;
     vm16 = (uint32_t)(__ballot(v) & 0xFFFFull);
@@ -329,10 +362,10 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     float S[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const uint32_t b = v ? ((cur.sc[u] >> (8 * g)) & 0xFFu) : 0u;
+      const uint32_t b = v ? cur.scale(u, g) : 0u;
       S[u] = __builtin_amdgcn_cvt_f32_fp8(b, 0);
     }
-    const u32x2 rope = cur.rope;
+    const auto rope = cur.rope;
     load_tail(cur, rec_next, hf, g);      // scales and RoPE of the next chunk
 #pragma unroll
     for (int b = 0; b < 2; b++) sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -340,12 +373,12 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     for (int j = 0; j < 8; j++) {
       const int u = j >> 1;
       const float Fv = __uint_as_float((__float_as_uint(S[u]) & 0x807FFFFFu) | 0x3F800000u);
-      const f16x2 F = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(Fv, Fv));   // exact
+      const f16x2 Fm = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(Fv, Fv));   // exact
       const uint32_t w = cur.nope[u >> 1][2 * (u & 1) + (j & 1)];
-      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 0) * F;
-      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 1) * F;
-      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 2) * F;
-      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 3) * F;
+      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 0) * Fm;
+      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 1) * Fm;
+      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 2) * Fm;
+      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 3) * Fm;
       const f16x8 k = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
       *reinterpret_cast<lds_f16x8*>((lds_u8*)(size_t)wbase + (((8 * g + j) ^ vsw) << 4)) = k;
 #pragma unroll
@@ -356,7 +389,15 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
       if (j == 3) load_nope(cur, 0, rec_next, hf, g);
       if (j == 7) load_nope(cur, 1, rec_next, hf, g);
     }
-    {
+    if constexpr (F::kBf16Rope) {
+      // bf16 RoPE straight from the record into a bf16 MFMA
+      const bf16x8 k = __builtin_bit_cast(bf16x8, rope);
+#pragma unroll
+      for (int b = 0; b < 2; b++) {
+        const bf16x8 qv = *reinterpret_cast<const lds_bf16x8*>(qlds + (((hf * 2 + b) * 9 + 8) * 64 + lane) * 16);
+        sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qv, sacc[b], 0, 0, 0);
+      }
+    } else {
       const f16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rope.x, 1.0f, false);
       const f16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rope.x, 1.0f, true);
       const f16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rope.y, 1.0f, false);
@@ -683,24 +724,27 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 
 size_t decode_w32_lds_bytes() { return kLdsBytes; }
 
-template <bool kDual>
+template <bool kDual, class F>
 static hipError_t launch_w32_kernel(const DecodeArgs& a, int grid, size_t lds, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel<kDual>,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel<kDual, F>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(decode_w32_kernel<kDual>, dim3(grid), dim3(64 * kWavesP), lds, stream, a);
+  hipLaunchKernelGGL((decode_w32_kernel<kDual, F>), dim3(grid), dim3(64 * kWavesP), lds, stream, a);
   return hipSuccess;
 }
 
 hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.rows * (a.h_q / 32) * a.splits;
   const size_t lds = decode_w32_lds_bytes();
-  hipError_t e0 = a.cache1 ? launch_w32_kernel<true>(a, grid, lds, stream)
-                           : launch_w32_kernel<false>(a, grid, lds, stream);
+  const bool f432 = a.pa.record_bytes == Fmt432::kBytes;
+  hipError_t e0 = a.cache1 ? (f432 ? launch_w32_kernel<true, Fmt432>(a, grid, lds, stream)
+                                   : launch_w32_kernel<true, Fmt352>(a, grid, lds, stream))
+                           : (f432 ? launch_w32_kernel<false, Fmt432>(a, grid, lds, stream)
+                                   : launch_w32_kernel<false, Fmt352>(a, grid, lds, stream));
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;

@@ -1,12 +1,17 @@
 // Device-side helpers shared by the codec, dequantize-gather and decode
-// kernels: the 352-byte record layout, exact E2M1/E4M3 -> bf16 dequantization
+// kernels: the two record layouts, exact E2M1/E4M3 -> bf16 dequantization
 // and slot -> record addressing.  gfx950 only.
 //
-// Record layout (FlashMLA PR #18 "W4A16 DSA: NVFP4 KV cache format for SM100
-// sparse decode", PR description): bytes [0,256) hold 512 E2M1 NoPE codes two
-// per byte (element 2j in the low nibble of byte j), [256,320) 64 unscaled
-// E4M3 RoPE values, [320,352) 32 E4M3 block scales with the scale of 16-element
-// block s at byte 320 + 8*(s&3) + (s>>2).
+// 352-byte record (FlashMLA PR #18 "W4A16 DSA: NVFP4 KV cache format for
+// SM100 sparse decode", PR description): bytes [0,256) hold 512 E2M1 NoPE
+// codes two per byte (element 2j in the low nibble of byte j), [256,320) 64
+// unscaled E4M3 RoPE values, [320,352) 32 E4M3 block scales with the scale of
+// 16-element block s at byte 320 + 8*(s&3) + (s>>2).
+//
+// 432-byte record (vLLM PR #82 "kv: nvfp4_ds_mla -- 4-bit NVFP4 KV cache for
+// B12X sparse MLA (SM120)", summary and Fix): the same NoPE codes in [0,256),
+// 32 E4M3 block scales in block order in [256,288), a zeroed 16-byte pad in
+// [288,304), and 64 bf16 RoPE values copied verbatim in [304,432).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,14 +19,11 @@
 
 namespace nvfp4 {
 
-constexpr int kRecordBytes = 352;
 constexpr int kNopeDim = 512;
 constexpr int kRopeDim = 64;
 constexpr int kQkDim = 576;
 constexpr int kVDim = 512;
 constexpr int kNopeBytes = 256;
-constexpr int kRopeOffset = 256;
-constexpr int kScaleOffset = 320;
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -34,6 +36,23 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 // Byte of the scale area holding NoPE block s (the 8x4 -> 4x8 transpose).
 __host__ __device__ constexpr int scale_byte(int s) { return 8 * (s & 3) + (s >> 2); }
+
+// Record formats as compile-time traits.
+struct Fmt352 {                      // E4M3 RoPE, permuted scales
+  static constexpr int kBytes = 352;
+  static constexpr int kScaleOff = 320;
+  static constexpr int kRopeOff = 256;
+  static constexpr bool kBf16Rope = false;
+  __host__ __device__ static constexpr int scale_at(int s) { return kScaleOff + scale_byte(s); }
+};
+struct Fmt432 {                      // bf16 RoPE, scales in block order, 16-byte pad
+  static constexpr int kBytes = 432;
+  static constexpr int kScaleOff = 256;
+  static constexpr int kPadOff = 288;
+  static constexpr int kRopeOff = 304;
+  static constexpr bool kBf16Rope = true;
+  __host__ __device__ static constexpr int scale_at(int s) { return kScaleOff + s; }
+};
 
 // Two packed bf16 from the upper halves of two fp32 values.  Exact whenever
 // both values are bf16-representable (true for every dequantized value).
@@ -72,7 +91,8 @@ __device__ __forceinline__ void dequant8(uint32_t nib, float scale, uint32_t out
 }
 
 // Slot -> byte offset of its record in the paged cache.  Pages of
-// `block_size` records start every `block_stride` bytes.  Power-of-two page
+// `block_size` records of `record_bytes` each start every `block_stride`
+// bytes.  Power-of-two page
 // sizes use shift/mask; others use a 64-bit reciprocal (exact for every
 // 32-bit slot: floor(n * ceil(2^64/d) / 2^64) == n / d).
 struct PageAddr {
@@ -81,6 +101,7 @@ struct PageAddr {
   uint32_t block_size;
   uint32_t shift;        // log2(block_size) when pow2
   uint32_t pow2;
+  uint32_t record_bytes; // 352 or 432
   __device__ __forceinline__ uint64_t offset(uint32_t slot) const {
     uint32_t page, off;
     if (pow2) {
@@ -93,7 +114,7 @@ struct PageAddr {
       page = (uint32_t)__umul64hi((uint64_t)slot, recip);
       off = slot - page * block_size;
     }
-    return (uint64_t)page * block_stride + (uint64_t)off * kRecordBytes;
+    return (uint64_t)page * block_stride + (uint64_t)off * record_bytes;
   }
 };
 

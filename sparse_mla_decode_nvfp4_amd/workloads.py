@@ -97,6 +97,7 @@ class DecodeWorkload:
     new_slots: np.ndarray                # int64 [B * S_q]
     description: str = ""
     extra: dict = field(default_factory=dict)
+    record_bytes: int = RECORD_BYTES     # 352, or 432 for the nvfp4_ds_mla record
 
     @property
     def num_slots(self):
@@ -176,6 +177,15 @@ def decode_h64(rep=0, batch=32, with_latents=True):
                    1.0 / 24.0, idx, new_slots, True,
                    f"h_q 64: B{batch} S_q1, 32768-token contexts, topk 2048, "
                    "5% invalid, sink", rep, with_latents=with_latents)
+
+
+def decode_h64_ds_mla(rep=0, batch=32, with_latents=True):
+    """decode_h64's inputs over a cache of 432-byte nvfp4_ds_mla records."""
+    wl = decode_h64(rep=rep, batch=batch, with_latents=with_latents)
+    wl.name = "decode_h64_ds_mla"
+    wl.record_bytes = 432
+    wl.description = wl.description.replace("h_q 64:", "h_q 64, 432-byte records:")
+    return wl
 
 
 def decode_h128_varlen(rep=0, batch=64, with_latents=True):
@@ -359,6 +369,7 @@ DECODE_WORKLOADS = {
     "decode_h64": decode_h64,
     "decode_h128_varlen": decode_h128_varlen,
     "decode_h16_mtp": decode_h16_mtp,
+    "decode_h64_ds_mla": decode_h64_ds_mla,
 }
 
 DUAL_WORKLOADS = {

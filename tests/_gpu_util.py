@@ -61,7 +61,7 @@ def oracle_records_from_workload(wl):
 
     def fn(slots):
         rows = wl.slot_rows(slots)
-        return OC.quantize_records(f64(lat[rows]), f64(rope[rows]))
+        return OC.quantize_records(f64(lat[rows]), f64(rope[rows]), wl.record_bytes)
     return fn
 
 

@@ -34,25 +34,28 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = m.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), name
         assert name in m.SIGNATURES, name
     assert m.abi_version() == 1
 
 
-def test_check_format_accepts_only_the_352_byte_record():
+def test_check_format_accepts_the_352_and_432_byte_records():
     m.check_format()
+    m.check_format(record_bytes=432)
     lib = m.lib()
-    for args in [(656, 512, 64, 512), (584, 512, 64, 512), (432, 512, 64, 512),
-                 (352, 448, 64, 512), (352, 512, 128, 512), (352, 512, 64, 576)]:
+    for args in [(656, 512, 64, 512), (584, 512, 64, 512), (384, 512, 64, 512),
+                 (352, 448, 64, 512), (352, 512, 128, 512), (352, 512, 64, 576),
+                 (432, 512, 64, 576)]:
         assert lib.nvfp4_mla_check_format(*args) == m.ERR_UNSUPPORTED_FORMAT
         assert "unsupported format" in m.last_error()
 
 
 def qa(fn="nvfp4_mla_quantize_append", **kw):
+    rb = 432 if fn.endswith("ds_mla") else 352
     a = dict(latent=P16, lstride=512, rope=P16, rstride=64, slots=P16, n=4, cache=P16,
-             nblocks=4, bs=64, stride=64 * 352, stream=NULL)
+             nblocks=4, bs=64, stride=64 * rb, stream=NULL)
     a.update(kw)
     return getattr(m.lib(), fn)(a["latent"], a["lstride"], a["rope"], a["rstride"],
                                 a["slots"], a["n"], a["cache"], a["nblocks"],
@@ -75,10 +78,26 @@ def qa(fn="nvfp4_mla_quantize_append", **kw):
     (dict(lstride=520 + 4), "16-byte aligned"),
     (dict(latent=ctypes.c_void_p(0x100004)), "16-byte aligned"),
 ])
-@pytest.mark.parametrize("fn", ["nvfp4_mla_quantize_append", "nvfp4_mla_quantize_append_fp16"])
+@pytest.mark.parametrize("fn", ["nvfp4_mla_quantize_append", "nvfp4_mla_quantize_append_fp16",
+                                "nvfp4_mla_quantize_append_ds_mla"])
 def test_quantize_append_rejects_bad_arguments(fn, kw, needle):
+    if fn.endswith("ds_mla") and "stride" in kw:
+        kw = dict(stride=kw["stride"] // 352 * 432 + kw["stride"] % 352)
     assert qa(fn, **kw) == m.ERR_INVALID_ARGUMENT
     assert needle in m.last_error()
+
+
+def test_ds_mla_exports_check_the_432_byte_page_stride():
+    # a stride that holds 64 records of 352 bytes but not of 432
+    assert qa("nvfp4_mla_quantize_append_ds_mla", stride=64 * 352) == m.ERR_INVALID_ARGUMENT
+    assert "block_size * 432" in m.last_error()
+    assert m.lib().nvfp4_mla_dequantize_gather_ds_mla(P16, 4, 64, 64 * 352, P16, 3, P16,
+                                                      NULL) == m.ERR_INVALID_ARGUMENT
+    assert "block_size * 432" in m.last_error()
+    assert m.lib().nvfp4_mla_sparse_decode_ds_mla(
+        P16, P16, 4, 64, 64 * 352, P16, 2, 1, 16, 64, NULL, 0.04, P16, P16, NULL, 0, 1,
+        NULL) == m.ERR_INVALID_ARGUMENT
+    assert "block_size * 432" in m.last_error()
 
 
 def dec(**kw):

@@ -147,7 +147,7 @@ def full_workload(lib, wl, sample_rows):
     expected values from the oracle quantizing the same latents."""
     note(f"{wl.name}: rows={wl.batch * wl.s_q} h={wl.h_q} topk={wl.topk} "
          f"slots={wl.num_slots} filled={len(wl.slots)}")
-    cache = lib.new_cache(wl.num_blocks, wl.block_size, DEV)
+    cache = lib.new_cache(wl.num_blocks, wl.block_size, DEV, record_bytes=wl.record_bytes)
     lib.quantize_append(wl.latent.to(DEV), wl.rope.to(DEV),
                         torch.from_numpy(wl.slots).to(DEV), cache)
     splits = lib.plan(wl.batch, wl.s_q, wl.h_q, wl.topk)
@@ -177,6 +177,7 @@ def test_tiny_workload_all_rows(lib):
     ("decode_h64", [0, 1, 7, 15, 16, 30, 31]),
     ("decode_h128_varlen", [0, 5, 17, 33, 48, 62, 63]),
     ("decode_h16_mtp", [0, 1, 2, 3, 100, 101, 255, 256, 400, 510, 511]),
+    ("decode_h64_ds_mla", [0, 3, 8, 15, 24, 31]),
 ])
 def test_full_size_workloads(lib, name, rows):
     wl = W.DECODE_WORKLOADS[name]()

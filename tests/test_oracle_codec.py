@@ -187,3 +187,54 @@ def test_quantize_append_leaves_unmapped_slots_untouched():
     assert np.array_equal(out[sm[keep]], C.quantize_records(x[keep], r[keep]))
     untouched = np.setdiff1d(np.arange(64), sm[keep])
     assert np.array_equal(out[untouched], cache[untouched])
+
+
+def ds_tokens(n=64, rep=0):
+    lat, rope = W.latents(0, n, rep=rep)
+    return lat, rope, lat.to(torch.float64).numpy(), rope.to(torch.float64).numpy()
+
+
+def test_ds_mla_record_meets_the_pages_test_invariants():
+    """[vLLM-82] test commit, on the 432-byte record itself: scales within half
+    a mantissa step of amax/6, NoPE error at most 1.25x the group scale
+    (normal scales), the 16-byte pad zero, the RoPE lane the input's bf16 bits
+    verbatim (compared with torch's own bf16 bit patterns)."""
+    lat, rope, x, r = ds_tokens(256)
+    rec = C.quantize_records(x, r, F.DS_RECORD_BYTES)
+    assert rec.shape == (256, 432)
+    sv = F.e4m3_decode(C.record_scale_bytes(rec))
+    amax = np.abs(x.reshape(-1, 32, 16)).max(-1)
+    normal = sv >= 2.0 ** -6
+    assert np.all(np.abs(sv - amax / 6)[normal] <= (amax / 6)[normal] / 16 + 1e-300)
+    deq = C.dequantize_records(rec)
+    err = np.abs(deq[:, :512] - x).reshape(-1, 32, 16).max(-1)
+    assert np.all(err[normal] <= 1.25 * sv[normal])
+    assert np.all(rec[:, 288:304] == 0)
+    torch_bits = rope.contiguous().view(torch.int16).numpy().view(np.uint8).reshape(256, 128)
+    assert np.array_equal(rec[:, 304:432], torch_bits)
+    assert np.array_equal(deq[:, 512:], r)
+
+
+def test_ds_mla_and_352_records_share_codes_and_scales():
+    """The two records differ only in where the scales sit and how RoPE is
+    stored: the NoPE bytes are identical and the 432-byte record's scale byte
+    256 + s equals the 352-byte record's byte 320 + 8(s&3) + (s>>2)."""
+    _, _, x, r = ds_tokens(64, rep=3)
+    a = C.quantize_records(x, r)
+    b = C.quantize_records(x, r, F.DS_RECORD_BYTES)
+    assert np.array_equal(a[:, :256], b[:, :256])
+    for s in range(32):
+        assert np.array_equal(b[:, 256 + s], a[:, 320 + 8 * (s & 3) + (s >> 2)])
+    assert np.array_equal(C.dequantize_records(a)[:, :512], C.dequantize_records(b)[:, :512])
+
+
+def test_ds_mla_append_leaves_unmapped_slots_untouched():
+    rng = np.random.default_rng(5)
+    cache = rng.integers(0, 256, size=(50, 432), dtype=np.uint8)
+    _, _, x, r = ds_tokens(8, rep=4)
+    sm = np.array([3, -1, 49, 0, 7, -1, 20, 21])
+    out = C.quantize_append(cache, x, r, sm)
+    keep = sm >= 0
+    assert np.array_equal(out[sm[keep]], C.quantize_records(x[keep], r[keep], F.DS_RECORD_BYTES))
+    untouched = np.setdiff1d(np.arange(50), sm[keep])
+    assert np.array_equal(out[untouched], cache[untouched])

@@ -16,11 +16,12 @@ import torch
 from oracle import formats as F
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "record_layout.txt")
+GOLDEN_DS = os.path.join(os.path.dirname(__file__), "golden", "record_layout_ds_mla.txt")
 
 
-def golden():
+def golden(path=GOLDEN):
     out = {}
-    for line in open(GOLDEN):
+    for line in open(path):
         line = line.split("#", 1)[0].strip()
         if line:
             k, v = (t.strip() for t in line.split("=", 1))
@@ -143,3 +144,31 @@ def test_e2m1_ties_go_to_even_codes():
     # above 6 saturates; exactly 6 is code 7
     assert F.nearest_code(np.array([7.0]), 1.0, F.E2M1_GRID)[0] == 7
     assert F.nearest_code(np.array([6.0]), 1.0, F.E2M1_GRID)[0] == 7
+
+
+def test_ds_mla_record_layout_matches_pages():
+    g = golden(GOLDEN_DS)
+    sizes = dict(nope=int(g["nope_bytes"]), scales=int(g["scale_bytes"]),
+                 pad=int(g["pad_bytes"]), rope=int(g["rope_bytes"]))
+    assert sum(sizes.values()) == int(g["record_bytes"]) == F.DS_RECORD_BYTES
+    starts, off = {}, 0
+    for name in g["region_order"].split():
+        starts[name] = off
+        off += sizes[name]
+    assert starts["nope"] == F.NOPE_OFFSET and sizes["nope"] == F.NOPE_BYTES
+    assert starts["scales"] == F.DS_SCALE_OFFSET and sizes["scales"] == F.N_GROUPS
+    assert starts["pad"] == F.DS_PAD_OFFSET and sizes["pad"] == F.DS_PAD_BYTES
+    assert starts["rope"] == F.DS_ROPE_OFFSET and sizes["rope"] == 2 * F.ROPE_DIM
+    assert int(g["scale_group_elements"]) == F.GROUP
+    assert sum(int(t) for t in g["fp8_ds_mla_regions"].split()) == int(g["fp8_ds_mla_record_bytes"])
+
+
+def test_bf16_decode_matches_torch_all_65536():
+    bits = np.arange(1 << 16, dtype=np.int64)
+    ours = F.bf16_decode(bits)
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref, equal_nan=True)
+    num = ~np.isnan(ref)                       # a NaN's sign carries nothing
+    assert np.array_equal(np.signbit(ours[num]), np.signbit(ref[num]))
+    fin = np.isfinite(ref)
+    assert np.array_equal(F.bf16_bits(ref[fin]).astype(np.int64), bits[fin])
