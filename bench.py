@@ -54,6 +54,9 @@ def parse():
                         "captured and checked against the eager results)")
     p.add_argument("--only", default=None, help="run just this workload (profiling)")
     p.add_argument("--splits", type=int, default=0, help="override the planner's split count")
+    p.add_argument("--prefill-sweep", action="store_true",
+                   help="time the sparse prefill over the pages' operator grid (heads per rank "
+                        "x query tokens) and print one JSON line with the table")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -142,8 +145,8 @@ def decode_kernel_name(h_q):
 def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_splits=0):
     import torch
     t_gen = time.time()
-    dual = name in W.DUAL_WORKLOADS
-    gen = W.DUAL_WORKLOADS[name] if dual else W.DECODE_WORKLOADS[name]
+    dual = W.dual_workload(name) is not None
+    gen = W.dual_workload(name) if dual else W.DECODE_WORKLOADS[name]
     sets = [gen(rep=r, with_latents=False) for r in range(nsets)]
     wl = sets[0]
     pools = [wl.primary, wl.extra_pool] if dual else [wl]
@@ -364,6 +367,18 @@ def main():
     lib.lib()                      # fails loudly when the HIP library is missing
     use_graph = args.graph
 
+    if args.prefill_sweep:
+        table = []
+        for h in W.PREFILL_HEADS:
+            for t in W.PREFILL_TOKENS:
+                r = bench_decode(lib, W, f"prefill_dual_h{h}_t{t}", args.steps, args.warmup, 1,
+                                 use_graph, dev)
+                table.append({k: r[k] for k in ("workload", "h_q", "rows", "splits", "kernel",
+                                                "decode_ms_mean", "decode_tflops", "mfma_frac",
+                                                "decode_hbm_gbps")})
+        print(json.dumps({"prefill_sweep": table, "steps": args.steps, "warmup": args.warmup}))
+        return
+
     if args.only:
         if args.only in ("append_write", "append_write_fp16"):
             res = bench_append(lib, W, args.steps, args.warmup, dev, fp16=args.only.endswith("fp16"))
@@ -381,6 +396,10 @@ def main():
             if name != args.workload:
                 extra[name] = bench_decode(lib, W, name, max(20, args.steps // 2),
                                            max(5, args.warmup // 2), args.sets, use_graph, dev)
+        # the prefill's 4096 query rows already span the pool: one index set
+        extra["prefill_dual_h64_t4096"] = bench_decode(lib, W, "prefill_dual_h64_t4096",
+                                                       max(20, args.steps // 4),
+                                                       max(5, args.warmup // 4), 1, use_graph, dev)
         extra["append_write"] = bench_append(lib, W, max(20, args.steps // 2),
                                              max(5, args.warmup // 2), dev)
         extra["append_write_fp16"] = bench_append(lib, W, max(20, args.steps // 2),

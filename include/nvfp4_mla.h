@@ -189,16 +189,11 @@ int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q,
  * num_splits == 1).  num_splits == 0 means "what the planner picks".
  * Returns 0 and sets the error on invalid arguments.
  *
- * The workspace holds the splits' partial O and LSE and one arrival counter
- * per (query row, group of 16 heads).  When h_q is a multiple of 32 a
- * combine kernel launched right after the decode merges the partials;
- * otherwise the last split to finish merges them inside the decode kernel
- * (the counters serve that).  The caller zero-fills a workspace
- * before its first use with a given (batch, s_q, h_q, num_splits); every
- * completed decode leaves the counters zero again, so further decodes of
- * that shape reuse it without clearing (a different shape needs a fresh
- * zero fill, since the counters move).  Decodes that may run concurrently
- * need separate workspaces.
+ * The workspace holds the splits' partial O and LSE, which a combine kernel
+ * launched right after the decode merges.  It needs no initialisation and
+ * keeps nothing between calls, so one workspace serves every later decode
+ * whose size it covers.  Decodes that may run concurrently need separate
+ * workspaces.
  */
 size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
                                               int32_t h_q, int32_t topk,
@@ -225,8 +220,8 @@ size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
  *              bytes (may be NULL when that size is 0); 256-byte aligned
  *   num_splits 0 = planner's choice, else 1..NVFP4_MLA_MAX_SPLITS
  * h_q must be a multiple of 16 (1..16 * 16), topk in [1, 65536].
- * The decode is one kernel launch, plus one combine launch when h_q is a
- * multiple of 32 and more than one split runs.
+ * The decode is one kernel launch, plus one combine launch when more than
+ * one split runs.
  */
 int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int64_t num_blocks, int32_t block_size,

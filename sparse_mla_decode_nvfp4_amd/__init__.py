@@ -200,7 +200,7 @@ def plan(batch, s_q, h_q, topk):
 
 
 def workspace_size(batch, s_q, h_q, topk, num_splits=0):
-    """Bytes of decode workspace; allocate it zero-filled (torch.zeros) once."""
+    """Bytes of decode workspace (no initialisation needed; reusable)."""
     n = lib().nvfp4_mla_sparse_decode_workspace_size(batch, s_q, h_q, topk, num_splits)
     err = last_error()
     if err:
@@ -226,8 +226,7 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
         num_splits = plan(b, s, h, topk)
     need = workspace_size(b, s, h, topk, num_splits)
     if need and workspace is None:
-        # zero-filled once: the split-merge counters must start at zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -266,7 +265,7 @@ def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, soft
         num_splits = plan(b, s, h, topk0 + topk1)
     need = workspace_size(b, s, h, topk0 + topk1, num_splits)
     if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
     if lse is None:

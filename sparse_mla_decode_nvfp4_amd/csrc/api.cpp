@@ -157,23 +157,20 @@ int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
 //   o_part   [splits, rows, h_q, 512] fp32 (the 32-head kernel fills the first half
 //            of it with fp16 partials)
 //   lse_part [splits, rows, h_q] fp32
-//   counters [rows, h_q/16] uint32 -- zero on entry, left zero on exit
 struct WsLayout {
-  size_t o_off, lse_off, cnt_off, total;
+  size_t o_off, lse_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(int64_t rows, int32_t h_q, int32_t splits) {
-  WsLayout w{0, 0, 0, 0};
+  WsLayout w{0, 0, 0};
   if (splits <= 1) return w;
   const size_t o = (size_t)splits * rows * h_q * NVFP4_MLA_V_DIM * sizeof(float);
   const size_t l = (size_t)splits * rows * h_q * sizeof(float);
-  const size_t c = (size_t)rows * (h_q / 16) * sizeof(uint32_t);
   w.o_off = 0;
   w.lse_off = align256(o);
-  w.cnt_off = w.lse_off + align256(l);
-  w.total = w.cnt_off + align256(c);
+  w.total = w.lse_off + align256(l);
   return w;
 }
 
@@ -315,7 +312,6 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
     char* base = static_cast<char*>(workspace);
     a.o_part = reinterpret_cast<float*>(base + w.o_off);
     a.lse_part = reinterpret_cast<float*>(base + w.lse_off);
-    a.counters = reinterpret_cast<uint32_t*>(base + w.cnt_off);
   }
   hipError_t e = nvfp4::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)

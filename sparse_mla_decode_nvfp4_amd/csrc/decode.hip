@@ -33,11 +33,13 @@
 //   * indices are prefetched two tiles ahead and token bytes one tile ahead;
 //   * the running max is only raised (and O rescaled) when a tile exceeds it
 //     by more than 2^8, so rescales are rare.
-// With several splits, the last split of a (row, head group) to finish merges
-// the partial results (LSE-weighted) inside the same launch.
+// With several splits, each split writes its partial result (fp32 O
+// normalised within the split, and its LSE) and the combine kernel, launched
+// right after, merges them: the launch boundary makes the partials visible
+// across XCDs, where an in-kernel merge needs device-scope fences that write
+// back and invalidate L2.
 #include <math.h>
 
-#include "combine_math.h"
 #include "device_common.h"
 #include "kv_source.h"
 #include "launch.h"
@@ -167,7 +169,6 @@ decode_tile16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ptile[16][kPRow];
   __shared__ float tmax[kWaves][16];
   __shared__ float lsum[kWaves][16];
-  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -437,32 +438,6 @@ decode_tile16_kernel(DecodeArgs a) {
     if (a.splits == 1) a.lse[orow + n] = lse;
     else a.lse_part[prow + n] = lse;
   }
-  if (a.splits == 1) return;
-
-  // ---- split-KV: the last split of this (row, head group) to finish merges
-  // all splits' partials.  Release the partials device-wide, count, and let
-  // the last arrival acquire them; it resets the counter for the next call.
-  // The workgroup barrier completes every wave's partial stores (to this
-  // XCD's L2); one thread then releases them device-wide, counts, and on the
-  // last arrival acquires the other splits' partials for the whole CU.
-  __syncthreads();
-  uint32_t* counter = a.counters + (size_t)row * hgroups + hg;
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const bool last = atomicAdd(counter, 1u) == (uint32_t)(a.splits - 1);
-    if (last) __threadfence();
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  const int64_t rh0 = (int64_t)row * a.h_q + h0;
-  const int64_t part_stride = (int64_t)a.rows * a.h_q;
-  for (int e = threadIdx.x; e < 16 * (kVDim / 4); e += 64 * kWaves) {
-    const int h = e / (kVDim / 4);
-    combine_chunk4(a.o_part, a.lse_part, a.splits, part_stride, rh0 + h, 4 * (e % (kVDim / 4)),
-                   a.sink != nullptr ? a.sink + h0 + h : nullptr, a.out, a.lse);
-  }
-  if (threadIdx.x == 0) *counter = 0u;
 }
 
 bool decode_uses_w32(int32_t h_q) { return h_q % 32 == 0; }
@@ -480,7 +455,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_tile16_kernel<false, Fmt432>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_tile16_kernel<false, Fmt352>), dim3(grid), dim3(64 * kWaves), 0, stream, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_combine(a.o_part, a.lse_part, a.splits, a.rows, a.h_q, a.sink, a.out, a.lse, stream);
 }
 
 }  // namespace nvfp4

@@ -42,16 +42,16 @@ struct DecodeArgs {
   float scale_log2;         // softmax_scale * log2(e)
   uint16_t* out;            // [rows, h_q, 512] bf16
   float* lse;               // [rows, h_q]
-  float* o_part;            // [splits, rows, h_q, 512] fp32 (splits > 1)
+  float* o_part;            // [splits, rows, h_q, 512] (splits > 1): fp32, or fp16
+                            // in its first half from the 32-head kernel
   float* lse_part;          // [splits, rows, h_q]
-  uint32_t* counters;       // [rows, h_q/16], zero on entry and on exit
   int32_t splits;
 };
 
 // Decode launch: head counts that are multiples of 32 run the 32-head-group
-// kernel (decode_w32.hip), whose split-KV partials the combine kernel merges
-// right after; other head counts run the 16-head tile kernel (decode.hip),
-// which merges its partials in-kernel (last-arriving workgroup per row).
+// kernel (decode_w32.hip), other head counts the 16-head tile kernel
+// (decode.hip); with several splits the combine kernel merges their partials
+// right after.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream);
 bool decode_uses_w32(int32_t h_q);

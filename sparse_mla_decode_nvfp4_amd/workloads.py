@@ -364,6 +364,63 @@ def decode_h16_mtp_dual(rep=0, batch=256, with_latents=True, extra_block_size=2)
         f"window (64-token pages) + extra 512 history ({bs1}-token pages), 3% invalid, sink")
 
 
+def _distinct(r, n, k):
+    """k distinct integers of [0, n) in random order (n >= k): a batch of
+    draws with replacement, duplicates dropped, topped up until k remain;
+    O(k) where choice(n, k, replace=False) is O(n)."""
+    got = np.empty(0, dtype=np.int64)
+    while len(got) < k:
+        got = np.unique(np.concatenate([got, r.integers(0, n, size=k + k // 4 + 8)]))
+    return got[r.permutation(len(got))[:k]]
+
+
+def prefill_dual(rep=0, tokens=4096, h_q=64, seq=65536, with_latents=True, extra_block_size=64):
+    """Sparse prefill as the pages benchmark it: one sequence of `seq` tokens
+    whose last `tokens` positions are the query tokens (batch 1, s_q =
+    tokens), each attending, with one softmax, to its 128-token sliding
+    window (primary cache, 64-token pages) and to 512 distinct positions
+    drawn from before its window (extra cache, the whole sequence in
+    `extra_block_size`-token pages).  3 % of each list invalid; sink; Q
+    N(0,1) for `h_q` heads."""
+    cid, bs0, win, extra_k = 6, 64, 128, 512
+    bs1 = extra_block_size
+    first = seq - tokens                        # position of the first query token
+    base = ((first - win + 1) // bs0) * bs0     # the primary pool starts at a page boundary
+    r6 = _rng(cid, 6, 0)
+    t0, total0 = _page_table(r6, [-(-(seq - base) // bs0)])
+    t1, total1 = _page_table(r6, [-(-seq // bs1)])
+    r4 = _rng(cid, 4, rep)
+    idx0 = np.empty((1, tokens, win), dtype=np.int64)
+    idx1 = np.empty((1, tokens, extra_k), dtype=np.int64)
+    new_slots = np.empty(tokens, dtype=np.int64)
+    for j in range(tokens):
+        p = first + j
+        window = np.arange(p - win + 1, p + 1) - base
+        idx0[0, j] = t0[0][window // bs0] * bs0 + window % bs0
+        hist = _distinct(r4, p - win + 1, extra_k)
+        idx1[0, j] = t1[0][hist // bs1] * bs1 + hist % bs1
+        new_slots[j] = t0[0][(p - base) // bs0] * bs0 + (p - base) % bs0
+    idx0[r4.random(idx0.shape) < 0.03] = -1
+    idx1[r4.random(idx1.shape) < 0.03] = -1
+    # Q drawn in float32 directly (up to 8192 x 64 x 576 values)
+    q = torch.from_numpy(_rng(cid, 3, rep).standard_normal((1, tokens, h_q, QK_DIM),
+                                                           dtype=np.float32)).to(torch.bfloat16)
+    sink = _rng(cid, 5, 0).standard_normal(h_q).astype(np.float32)
+    slots0 = np.unique(np.concatenate([idx0[idx0 >= 0], new_slots]))
+    slots1 = np.unique(idx1[idx1 >= 0])
+    lat0 = rope0 = lat1 = rope1 = None
+    if with_latents:
+        lat0, rope0 = latents(cid, len(slots0), rep)
+        lat1, rope1 = latents(cid, len(slots1), rep, pool=1)
+    return DualDecodeWorkload(
+        f"prefill_dual_h{h_q}_t{tokens}", cid, 1, tokens, h_q, float(np.float32(1.0 / 24.0)), q,
+        sink, PagedPool(bs0, total0, slots0, lat0, rope0),
+        PagedPool(bs1, total1, slots1, lat1, rope1), idx0.astype(np.int32),
+        idx1.astype(np.int32), new_slots,
+        f"sparse prefill: {tokens} query tokens of a {seq}-token sequence, h_q {h_q}, "
+        f"primary 128-token window + extra 512 history ({bs1}-token pages), 3% invalid, sink")
+
+
 DECODE_WORKLOADS = {
     "tiny": tiny,
     "decode_h64": decode_h64,
@@ -374,4 +431,21 @@ DECODE_WORKLOADS = {
 
 DUAL_WORKLOADS = {
     "decode_h16_mtp_dual": decode_h16_mtp_dual,
+    "prefill_dual_h64_t4096": prefill_dual,
 }
+
+# the pages' operator benchmark grid: heads per rank x query tokens
+PREFILL_HEADS = (16, 32, 64)
+PREFILL_TOKENS = (64, 1024, 2048, 4096, 8192)
+
+
+def dual_workload(name):
+    """Generator of a dual-cache workload by name: the entries above, or
+    prefill_dual_h{H}_t{T} for any head count H and token count T."""
+    if name in DUAL_WORKLOADS:
+        return DUAL_WORKLOADS[name]
+    if name.startswith("prefill_dual_h") and "_t" in name:
+        h, t = name[len("prefill_dual_h"):].split("_t")
+        return lambda rep=0, with_latents=True: prefill_dual(rep=rep, tokens=int(t), h_q=int(h),
+                                                             with_latents=with_latents)
+    return None

@@ -201,8 +201,7 @@ def test_workspace_size_for_explicit_splits():
     al = lambda x: ((x + 255) // 256) * 256
     o = s * rows * h * 512 * 4                 # partial O
     lse = s * rows * h * 4                     # partial LSE
-    cnt = rows * (h // 16) * 4                 # split arrival counters
-    assert lib.nvfp4_mla_sparse_decode_workspace_size(4, 2, 16, 640, s) == al(o) + al(lse) + al(cnt)
+    assert lib.nvfp4_mla_sparse_decode_workspace_size(4, 2, 16, 640, s) == al(o) + al(lse)
 
 
 def test_empty_inputs_are_no_ops_after_validation():
