@@ -3,10 +3,13 @@
 
 One step = the whole hot path for one batch: quantize-append the step's new
 tokens (one per query row) into the paged NVFP4 cache, then the sparse decode
-(gather + dequant + QK + online softmax with sink + PV, split-KV merge inside
-the same kernel).  The headline workload is h_q 64 / batch 32 / top-k 2048;
-the h_q 16 MTP and h_q 128 varlen decode workloads and the 16384-token
-quantize-append are reported alongside.
+(gather + dequant + QK + online softmax with sink + PV, and the split-KV
+combine kernel when the planner splits).  The headline workload is h_q 64 /
+batch 32 / top-k 2048.  Reported alongside: the h_q 16 MTP decode (one cache
+and the dual-cache layout), the h_q 128 varlen decode, the h_q 64 decode over
+432-byte records, a 4096-token sparse prefill at h_q 64, and the 16384-token
+quantize-append from bf16 and fp16.  --prefill-sweep times the prefill over
+the pages' operator grid instead.
 
 Inputs are resident in HBM before timing starts: each pool is filled with
 NVFP4 records by the HIP quantize-append, and the timed loop rotates over R
@@ -383,7 +386,9 @@ def main():
         if args.only in ("append_write", "append_write_fp16"):
             res = bench_append(lib, W, args.steps, args.warmup, dev, fp16=args.only.endswith("fp16"))
         else:
-            res = bench_decode(lib, W, args.only, args.steps, args.warmup, args.sets, use_graph, dev,
+            # a prefill's query rows already span its pool: one index set
+            nsets = 1 if args.only.startswith("prefill") else args.sets
+            res = bench_decode(lib, W, args.only, args.steps, args.warmup, nsets, use_graph, dev,
                                args.splits)
         print(json.dumps(res))
         return
