@@ -35,15 +35,30 @@ constexpr int kWavesC = 4;
 // One wave per (row, head); lane l owns output dims 8l .. 8l+7.  Splits are
 // read four at a time (their LSEs and partials in flight together) and merged
 // against a running maximum of the LSEs, rescaling when it rises.  T is the
-// partial type: fp32 for the standalone export, fp16 for the 32-head decode's
-// own partials.
+// partial type: fp32 for the standalone export and the 16-head decode, fp16
+// for the 32-head decode's own partials.
+//
+// Workgroups are dealt to the 8 XCDs round-robin by blockIdx.  The decode
+// kernels run every workgroup of row r on XCD r % 8 when the row count is a
+// multiple of 8, so with xcd_rows the blocks of row r go there too and read
+// the partials from that XCD's L2.
 template <typename T>
 __global__ void __launch_bounds__(64 * kWavesC)
 combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
-               int32_t splits, int64_t rh_total, int32_t h_q, const float* __restrict__ sink,
-               uint16_t* __restrict__ out, float* __restrict__ lse) {
+               int32_t splits, int64_t rh_total, int32_t h_q, int32_t xcd_rows,
+               const float* __restrict__ sink, uint16_t* __restrict__ out,
+               float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * kWavesC + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t rh;
+  if (xcd_rows) {
+    const int64_t bpr = h_q / kWavesC;               // blocks per row
+    const int64_t i = blockIdx.x >> 3;
+    const int64_t row = (blockIdx.x & 7) + 8 * (i / bpr);
+    rh = row * h_q + kWavesC * (i % bpr) + w;
+  } else {
+    rh = (int64_t)blockIdx.x * kWavesC + w;
+  }
   if (rh >= rh_total) return;
   const int dv0 = 8 * lane;
   uint16_t* orow = out + rh * kVDim + dv0;
@@ -109,8 +124,10 @@ static hipError_t launch_combine_t(const T* o_part, const float* lse_part, int32
   const int64_t rh_total = rows * (int64_t)h_q;
   if (rh_total == 0) return hipSuccess;
   const int64_t blocks = (rh_total + kWavesC - 1) / kWavesC;
+  // XCD-matched placement needs whole rows per block and rows in eights
+  const int32_t xcd_rows = (rows % 8 == 0 && h_q % kWavesC == 0) ? 1 : 0;
   hipLaunchKernelGGL(combine_kernel<T>, dim3((uint32_t)blocks), dim3(64 * kWavesC), 0, stream,
-                     o_part, lse_part, splits, rh_total, h_q, sink, out, lse);
+                     o_part, lse_part, splits, rh_total, h_q, xcd_rows, sink, out, lse);
   return hipGetLastError();
 }
 

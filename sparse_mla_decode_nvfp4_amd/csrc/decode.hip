@@ -175,12 +175,27 @@ decode_tile16_kernel(DecodeArgs a) {
   const int g = lane >> 4;
   const int n = lane & 15;
 
+  // work unit (row, 16-head group, split).  Workgroups are dealt to the 8
+  // XCDs round-robin by blockIdx; when the row count allows, every workgroup
+  // of row r goes to XCD r % 8, so its head groups share the row's records
+  // and the combine kernel finds its partials in that XCD's L2.
   const int hgroups = a.h_q >> 4;
-  int bid = blockIdx.x;
-  const int split = bid % a.splits;
-  bid /= a.splits;
-  const int hg = bid % hgroups;
-  const int row = bid / hgroups;
+  int split, hg, row;
+  {
+    const int x = blockIdx.x;
+    if ((a.rows & 7) == 0) {
+      int y = x >> 3;
+      split = y % a.splits;
+      y /= a.splits;
+      hg = y % hgroups;
+      row = (y / hgroups) * 8 + (x & 7);
+    } else {
+      split = x % a.splits;
+      const int unit = x / a.splits;
+      hg = unit % hgroups;
+      row = unit / hgroups;
+    }
+  }
   const int h0 = hg * 16;
 
   // token range of this split, in whole tiles
