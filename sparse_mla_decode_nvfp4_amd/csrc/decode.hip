@@ -88,26 +88,55 @@ __device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, h16x2));
 }
 
-// The bytes one lane needs of one token record.  Lane group g takes eight
-// NoPE blocks whose scales are eight consecutive scale bytes: blocks 4c+g
-// (c = 0..7) in the 352-byte record, whose scale area is permuted, and blocks
-// 8g+c in the 432-byte record, whose scales are in block order.
+// The bytes one lane needs of one token record.  Lane group g takes NoPE
+// blocks 8g .. 8g+7: 64 contiguous bytes, four 16-byte loads (few, wide
+// gathers: the address unit, not HBM, limits this kernel's loads).  In the
+// 432-byte record their scales are the eight bytes 256 + 8g .. (block
+// order).  In the 352-byte record block s's scale sits at 320 + 8(s&3) +
+// (s>>2), so the lane's scales are the 16-bit words at 320 + 8k + 2g (k =
+// 0..3): word k holds blocks 8g+k (low byte) and 8g+4+k (high byte); the lane
+// loads the whole 32-byte scale area and picks them out.
 template <class F>
-struct RawTok {
-  u32x2 nope[8];         // NoPE block blk(g, c), c = 0..7
-  u32x2 scale;           // scale bytes 8g .. 8g+7 (= blocks blk(g, c))
+struct RawTok;
+template <>
+struct RawTok<Fmt352> {
+  u32x4 nope[4];         // NoPE bytes 64g + 16i .. +15
+  u32x4 sc[2];           // scale area, bytes 0 .. 31
   u32x4 rope;            // RoPE elements 16g .. 16g+15 (E4M3)
 };
 template <>
 struct RawTok<Fmt432> {
-  u32x2 nope[8];
-  u32x2 scale;
+  u32x4 nope[4];
+  u32x2 scale;           // scale bytes 8g .. 8g+7 (= blocks 8g .. 8g+7)
   u32x4 rope[2];         // RoPE elements 16g .. 16g+15 (bf16)
 };
 
 // NoPE block of lane group g's c-th k-step pair.
+__device__ __forceinline__ int blk(int g, int c) { return 8 * g + c; }
+
+// Scale bytes of blocks 8g .. 8g+3 (x) and 8g+4 .. 8g+7 (y), one byte each.
+__device__ __forceinline__ u32x2 block_scales(const RawTok<Fmt432>& t, int) { return t.scale; }
+__device__ __forceinline__ u32x2 block_scales(const RawTok<Fmt352>& t, int g) {
+  const bool second = (g >> 1) != 0;              // word in the second dword of its 8 bytes
+  const uint32_t sh = 16u * (uint32_t)(g & 1);
+  const uint32_t w0 = (second ? t.sc[0].y : t.sc[0].x) >> sh;
+  const uint32_t w1 = (second ? t.sc[0].w : t.sc[0].z) >> sh;
+  const uint32_t w2 = (second ? t.sc[1].y : t.sc[1].x) >> sh;
+  const uint32_t w3 = (second ? t.sc[1].w : t.sc[1].z) >> sh;
+  // byte i of perm(a, b, sel) is byte sel_i of the 8-byte value {a : b}
+  const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u) |
+                      (__builtin_amdgcn_perm(w3, w2, 0x0c0c0400u) << 16);
+  const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x0c0c0501u) |
+                      (__builtin_amdgcn_perm(w3, w2, 0x0c0c0501u) << 16);
+  return u32x2{lo, hi};
+}
+
+// The dword holding codes 8h .. 8h+7 of block 8g + c.
 template <class F>
-__device__ __forceinline__ int blk(int g, int c) { return F::kBf16Rope ? 8 * g + c : 4 * c + g; }
+__device__ __forceinline__ uint32_t nope_word(const RawTok<F>& t, int c, int h) {
+  const u32x4& q = t.nope[c >> 1];
+  return (c & 1) ? (h ? q.w : q.z) : (h ? q.y : q.x);
+}
 
 // Unconditional loads (uniform control flow keeps the prefetch in flight:
 // after a divergent load the compiler can only wait for every outstanding
@@ -115,16 +144,26 @@ __device__ __forceinline__ int blk(int g, int c) { return F::kBf16Rope ? 8 * g +
 // bytes are zeroed when consumed, so their NoPE values are exact zeros and
 // cannot carry NaN into P V, and their scores are masked.
 template <class F>
-__device__ __forceinline__ void load_tok(RawTok<F>& t, const uint8_t* rec, int g) {
-#pragma unroll
-  for (int c = 0; c < 8; c++) t.nope[c] = *reinterpret_cast<const u32x2*>(rec + 8 * blk<F>(g, c));
-  t.scale = *reinterpret_cast<const u32x2*>(rec + F::kScaleOff + 8 * g);
+__device__ __forceinline__ void load_tok_nope(RawTok<F>& t, const uint8_t* rec, int g, int i) {
+  t.nope[i] = *reinterpret_cast<const u32x4*>(rec + 64 * g + 16 * i);
+}
+template <class F>
+__device__ __forceinline__ void load_tok_tail(RawTok<F>& t, const uint8_t* rec, int g) {
   if constexpr (F::kBf16Rope) {
+    t.scale = *reinterpret_cast<const u32x2*>(rec + F::kScaleOff + 8 * g);
     t.rope[0] = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 32 * g);
     t.rope[1] = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 32 * g + 16);
   } else {
+    t.sc[0] = *reinterpret_cast<const u32x4*>(rec + F::kScaleOff);
+    t.sc[1] = *reinterpret_cast<const u32x4*>(rec + F::kScaleOff + 16);
     t.rope = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 16 * g);
   }
+}
+template <class F>
+__device__ __forceinline__ void load_tok(RawTok<F>& t, const uint8_t* rec, int g) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) load_tok_nope(t, rec, g, i);
+  load_tok_tail(t, rec, g);
 }
 
 
@@ -232,7 +271,7 @@ decode_tile16_kernel(DecodeArgs a) {
     u32x4 raw[18];
 #pragma unroll
     for (int ks = 0; ks < 16; ks++)
-      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * blk<F>(g, ks >> 1) + 8 * (ks & 1));
+      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * blk(g, ks >> 1) + 8 * (ks & 1));
 #pragma unroll
     for (int ks = 16; ks < 18; ks++)
       raw[ks] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
@@ -285,12 +324,10 @@ decode_tile16_kernel(DecodeArgs a) {
   float m_r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float l_part = 0.f;          // this lane's share of head n's denominator
 
-  // V tile addresses.  Write (k-step 2c+h): chunk 2 blk(g, c) + h (= 8c + 2g
-  // + h, or 16g + 2c + h), token my_tok.  Read (PV k-step ks, half hb, block
-  // nb): token 32ks + 8g + 4hb + (l%16)/4, chunk 16w + 2nb + ((l%4)>>1), byte
-  // 8(l&1).
-  constexpr int kVwStep = F::kBf16Rope ? 2 : 8;       // chunks between c and c+1
-  const uint32_t vw_base = (uint32_t)(size_t)(vtile + 2 * blk<F>(g, 0) * kVChunk + my_tok * 16);
+  // V tile addresses.  Write (k-step 2c+h): chunk 2 blk(g, c) + h = 16g + 2c
+  // + h, token my_tok.  Read (PV k-step ks, half hb, block nb): token 32ks +
+  // 8g + 4hb + (l%16)/4, chunk 16w + 2nb + ((l%4)>>1), byte 8(l&1).
+  const uint32_t vw_base = (uint32_t)(size_t)(vtile + 2 * blk(g, 0) * kVChunk + my_tok * 16);
   const uint32_t vr_base = (uint32_t)(size_t)(vtile + (16 * wave + ((lane & 3) >> 1)) * kVChunk +
                                              (8 * g + ((lane >> 2) & 3)) * 16 + 8 * (lane & 1));
 
@@ -298,13 +335,14 @@ decode_tile16_kernel(DecodeArgs a) {
   // tile t+1's; the loop below alternates the two buffers so the prefetched
   // bytes are never copied.
   auto step = [&](RawTok<F>& cur, RawTok<F>& nxt, int t) {
-    // ---- prefetch: indices two tiles ahead, token bytes one tile ahead
+    // ---- prefetch: indices two tiles ahead, token bytes one tile ahead.
+    // The scale and RoPE bytes are requested here and each NoPE piece inside
+    // the dequant loop below: the eight waves of a CU reach this point
+    // together after a barrier, and issuing all their gathers at once backs
+    // up the address unit for thousands of cycles.
     const int32_t idx_nn = load_idx(t + 2);
     const RecRef rn = resolve(idx_nxt, t + 1);
-    load_tok(nxt, rn.ptr, g);
-    // keep the prefetch at the top of the step: the scheduler would otherwise
-    // sink these loads below the dequant and shorten their lead time
-    __builtin_amdgcn_sched_barrier(0);
+    load_tok_tail(nxt, rn.ptr, g);
     const bool cur_valid = ok_cur;
     const uint64_t vmask = __ballot(cur_valid);
 
@@ -313,8 +351,9 @@ decode_tile16_kernel(DecodeArgs a) {
     // ---- dequantize this wave's 16 tokens k-step by k-step: each K operand
     // goes to the V tile (NoPE) and straight into S^T = K Q^T (two
     // accumulation chains)
-    const uint32_t scx = cur_valid ? cur.scale.x : 0u;
-    const uint32_t scy = cur_valid ? cur.scale.y : 0u;
+    const u32x2 bsc = block_scales(cur, g);
+    const uint32_t scx = cur_valid ? bsc.x : 0u;
+    const uint32_t scy = cur_valid ? bsc.y : 0u;
     const f32x2 s01 = e4m3x2_to_f32<0>(scx);
     const f32x2 s23 = e4m3x2_to_f32<1>(scx);
     const f32x2 s45 = e4m3x2_to_f32<0>(scy);
@@ -326,11 +365,15 @@ decode_tile16_kernel(DecodeArgs a) {
       const h16x2 Fm = mantissa_f16(sc[c]);
 #pragma unroll
       for (int h = 0; h < 2; h++) {
-        const h16x8 k = dequant8_f16(h ? cur.nope[c].y : cur.nope[c].x, sc[c], Fm);
+        const h16x8 k = dequant8_f16(nope_word(cur, c, h), sc[c], Fm);
         *reinterpret_cast<__attribute__((address_space(3))) h16x8*>(
-            (lds_b*)(size_t)vw_base + (kVwStep * c + h) * kVChunk) = k;
+            (lds_b*)(size_t)vw_base + (2 * c + h) * kVChunk) = k;
         if (h == 0) s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c], s_acc, 0, 0, 0);
         else s_acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c + 1], s_acc1, 0, 0, 0);
+      }
+      if (c & 1) {
+        load_tok_nope(nxt, rn.ptr, g, c >> 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the gathers spread out
       }
     }
     if constexpr (F::kBf16Rope) {

@@ -132,9 +132,14 @@ __device__ __forceinline__ int acc_row(int r, int kg) { return 8 * (r >> 2) + 4 
 // rows of a with the even rows of b; permlane32_swap(a, b) exchanges the
 // upper 32 lanes of a with the lower 32 of b.
 
-// max(a, b) as med3(a, b, +inf): the compiler adds no NaN canonicalisation
-// of lane-swapped operands (scores are finite for finite inputs)
-__device__ __forceinline__ float fmax_p(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+// max(a, b) as one v_max_f32: written as an instruction because the
+// compiler otherwise canonicalises both lane-swapped operands first (two
+// extra VALU ops per use).  Scores are finite or -inf, never NaN.
+__device__ __forceinline__ float fmax_p(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 // Per-head maximum (max_blocks) or sum (sum_blocks) over the four 16-lane
 // rows: x0, x1 hold this lane's block-0 and block-1 values (heads n and
@@ -350,11 +355,13 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   // the partial-S exchange; each raw piece is refilled with the next chunk's
   // bytes (raw index nxt_raw, loaded a chunk earlier) right after its use.
   f32x4 sacc[2];
-  uint32_t vm16 = 0;
+  uint32_t okbits = 0;   // bit r: token 4g+r of the current chunk takes part
   auto pre = [&](RawP<F>& cur, bool& cur_ok, int32_t& nxt_raw, int pos) {
     const int32_t nxt2_raw = load_idx(pos + 2);
     const bool v = cur_ok;
-    vm16 = (uint32_t)(__ballot(v) & 0xFFFFull);
+    // validity of tokens 4g..4g+3 (the rows of this lane's partial S^T),
+    // taken from the lanes that hold those tokens' bytes
+    okbits = ((uint32_t)__ballot(v) >> (4 * g)) & 0xFu;
     const RecRef rn = resolve_rec<kDual>(a, nxt_raw, chunk_ok(pos + 1), tok_pos(pos + 1), src.topk0);
     const uint8_t* const rec_next = rn.ptr;
     // block scales of this lane; zero for an invalid token, so its V row is
@@ -440,16 +447,11 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 #pragma unroll
       for (int r = 0; r < 4; r++) s[b][r] = sacc[b][r] + o4[r];
     }
-    // lane holds heads n, 16+n and tokens 4g+r; invalid tokens -> -inf.
-    // Token validity is uniform over each 16-lane row, so the select
-    // condition is a scalar lane mask.
+    // lane holds heads n, 16+n and tokens 4g+r; invalid tokens -> -inf
+    // (a per-lane select on okbits: no scalar mask building)
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      uint64_t keep = 0;
-#pragma unroll
-      for (int gg = 0; gg < 4; gg++)
-        keep |= ((vm16 >> (4 * gg + r)) & 1u) ? (0xFFFFull << (16 * gg)) : 0ull;
-      const bool ok = __builtin_amdgcn_inverse_ballot_w64(keep);
+      const bool ok = (okbits >> r) & 1u;
 #pragma unroll
       for (int b = 0; b < 2; b++) s[b][r] = ok ? s[b][r] : -INFINITY;
     }
