@@ -78,23 +78,29 @@ static_assert(32 * 4096 <= kOffStat, "merge slots overlap the statistics");
 // g): NoPE blocks s = 16hf + 4g + u (u = 0..3), 32 contiguous bytes; their
 // scales; RoPE dims 32hf + 8g .. +7.  In the 352-byte record block s's scale
 // sits at 320 + 8(s&3) + (s>>2), so the four are byte g of the dwords at
-// 320 + 8u + 4hf, and RoPE is 8 E4M3 bytes; in the 432-byte record they are
-// the four bytes of the dword at 256 + 16hf + 4g, and RoPE is 8 bf16.
+// 320 + 8u + 4hf: the lane loads the whole 32-byte scale area (two wide
+// gathers rather than four narrow ones), and RoPE is 8 E4M3 bytes; in the
+// 432-byte record they are the four bytes of the dword at 256 + 16hf + 4g,
+// and RoPE is 8 bf16.
 template <class F>
 struct RawP;
 template <>
 struct RawP<Fmt352> {
   u32x4 nope[2];
-  uint32_t sc[4];
+  u32x4 sc[2];           // the scale area: dword 2u + hf holds blocks 16hf + 4g + u
   u32x2 rope;
-  __device__ __forceinline__ uint32_t scale(int u, int g) const { return (sc[u] >> (8 * g)) & 0xFFu; }
+  __device__ __forceinline__ uint32_t scale(int u, int g, int hf) const {
+    const u32x4& q = sc[u >> 1];
+    const uint32_t d = (u & 1) ? (hf ? q.w : q.z) : (hf ? q.y : q.x);
+    return (d >> (8 * g)) & 0xFFu;
+  }
 };
 template <>
 struct RawP<Fmt432> {
   u32x4 nope[2];
   uint32_t sc;
   u32x4 rope;
-  __device__ __forceinline__ uint32_t scale(int u, int) const { return (sc >> (8 * u)) & 0xFFu; }
+  __device__ __forceinline__ uint32_t scale(int u, int, int) const { return (sc >> (8 * u)) & 0xFFu; }
 };
 
 template <class F>
@@ -102,9 +108,8 @@ __device__ __forceinline__ void load_nope(RawP<F>& r, int q, const uint8_t* rec,
   r.nope[q] = *reinterpret_cast<const u32x4*>(rec + 128 * hf + 32 * g + 16 * q);
 }
 __device__ __forceinline__ void load_tail(RawP<Fmt352>& r, const uint8_t* rec, int hf, int g) {
-#pragma unroll
-  for (int u = 0; u < 4; u++)
-    r.sc[u] = *reinterpret_cast<const uint32_t*>(rec + Fmt352::kScaleOff + 8 * u + 4 * hf);
+  r.sc[0] = *reinterpret_cast<const u32x4*>(rec + Fmt352::kScaleOff);
+  r.sc[1] = *reinterpret_cast<const u32x4*>(rec + Fmt352::kScaleOff + 16);
   r.rope = *reinterpret_cast<const u32x2*>(rec + Fmt352::kRopeOff + 32 * hf + 8 * g);
 }
 __device__ __forceinline__ void load_tail(RawP<Fmt432>& r, const uint8_t* rec, int hf, int g) {
@@ -369,7 +374,7 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     float S[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const uint32_t b = v ? cur.scale(u, g) : 0u;
+      const uint32_t b = v ? cur.scale(u, g, hf) : 0u;
       S[u] = __builtin_amdgcn_cvt_f32_fp8(b, 0);
     }
     const auto rope = cur.rope;
