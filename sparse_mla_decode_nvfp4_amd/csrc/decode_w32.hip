@@ -233,31 +233,38 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   const int c_begin = split * cps;
   const int c_end = min(nchunks, c_begin + cps);
   const int span = max(c_end - c_begin, 0);
-  const int my_n = (span + 3) >> 2;             // the same for all pairs
   const RowSource<kDual> src(a, row);
 
-  // joined-list position of token n of this pair's i-th chunk
-  auto tok_pos = [&](int i) { return (c_begin + pr + 4 * i) * kChunkP + n; };
+  // Chunks are numbered within the split and dealt in blocks of 18: pairs 0
+  // and 1 take 5 of each block (offsets p, p+4, p+8, p+12, 16+p), pairs 2 and
+  // 3 take 4 (p, p+4, p+8, p+12).  Pairs 0 and 1 are the first waves of their
+  // SIMDs, which issue first and run about 1.25 times as fast, so the pairs
+  // finish together; the fixed deal keeps the summation order, and so the
+  // result, the same on every run.  cid0..cid2 are this pair's chunks pos,
+  // pos+1 and pos+2.
+  const int kp = pr < 2 ? 5 : 4;
+  auto cid_of = [&](int i) {
+    const int blk = i / kp, j = i - blk * kp;
+    return 18 * blk + (j < 4 ? pr + 4 * j : 16 + pr);
+  };
+  int cid0 = cid_of(0), cid1 = cid_of(1), cid2 = cid_of(2);
+  // joined-list position of token n of chunk c
+  auto tok_pos = [&](int c) { return (c_begin + min(c, span)) * kChunkP + n; };
   // its index: the load is unconditional (clamped in bounds) and chunk_ok
   // marks the entries that exist; the two are combined a chunk after the
   // load, so no wait follows it
-  auto load_idx = [&](int i) -> int32_t {
-    return src.load(min(tok_pos(min(i, max(my_n - 1, 0))), a.topk - 1));
-  };
-  auto chunk_ok = [&](int i) -> bool {
-    const int c = c_begin + pr + 4 * i;
-    return i < my_n && c < c_end && c * kChunkP + n < a.topk;
-  };
+  auto load_idx = [&](int c) -> int32_t { return src.load(min(tok_pos(c), a.topk - 1)); };
+  auto chunk_ok = [&](int c) -> bool { return c < span && tok_pos(c) < a.topk; };
 
   // the first chunk's indices and records are requested before the Q
   // set-up below, which hides part of their latency
   RawP<F> buf;
   bool ok_cur = false;
   int32_t idx_nxt = -1;
-  if (my_n > 0) {
-    const int32_t idx0 = load_idx(0);
-    idx_nxt = load_idx(1);
-    const RecRef r = resolve_rec<kDual>(a, idx0, chunk_ok(0), tok_pos(0), src.topk0);
+  if (cid0 < span) {
+    const int32_t idx0 = load_idx(cid0);
+    idx_nxt = load_idx(cid1);
+    const RecRef r = resolve_rec<kDual>(a, idx0, chunk_ok(cid0), tok_pos(cid0), src.topk0);
     ok_cur = r.ok;
     load_nope(buf, 0, r.ptr, hf, g);
     load_nope(buf, 1, r.ptr, hf, g);
@@ -362,12 +369,12 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   f32x4 sacc[2];
   uint32_t okbits = 0;   // bit r: token 4g+r of the current chunk takes part
   auto pre = [&](RawP<F>& cur, bool& cur_ok, int32_t& nxt_raw, int pos) {
-    const int32_t nxt2_raw = load_idx(pos + 2);
+    const int32_t nxt2_raw = load_idx(cid2);
     const bool v = cur_ok;
     // validity of tokens 4g..4g+3 (the rows of this lane's partial S^T),
     // taken from the lanes that hold those tokens' bytes
     okbits = ((uint32_t)__ballot(v) >> (4 * g)) & 0xFu;
-    const RecRef rn = resolve_rec<kDual>(a, nxt_raw, chunk_ok(pos + 1), tok_pos(pos + 1), src.topk0);
+    const RecRef rn = resolve_rec<kDual>(a, nxt_raw, chunk_ok(cid1), tok_pos(cid1), src.topk0);
     const uint8_t* const rec_next = rn.ptr;
     // block scales of this lane; zero for an invalid token, so its V row is
     // zero
@@ -539,12 +546,15 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 #pragma unroll
     for (int nb = 0; nb < 8; nb++) acc_o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, z, zc, 0, 0, 0);
   }
-  if (my_n > 0) {
-    for (int pos = 0; pos < my_n; pos++) {
-      pre(buf, ok_cur, idx_nxt, pos);
-      pair_wait(pos);
-      post(pos);
-    }
+  // both halves of a pair hold the same chunk ids, so they run the same
+  // iterations
+  for (int pos = 0; cid0 < span; pos++) {
+    pre(buf, ok_cur, idx_nxt, pos);
+    pair_wait(pos);
+    post(pos);
+    cid0 = cid1;
+    cid1 = cid2;
+    cid2 = cid_of(pos + 3);
   }
 
   // ---- merge the four pairs (same heads and output dims, disjoint tokens)
