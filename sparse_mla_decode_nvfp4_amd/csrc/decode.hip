@@ -263,56 +263,77 @@ decode_tile16_kernel(DecodeArgs a) {
 
   // ---- Q^T operand registers (head n, k-chunk g) in fp16 with a per-head
   // power-of-two scale; a negative softmax scale flips Q's sign (exact), so
-  // the score scale is positive
+  // the score scale is positive.  The workgroup converts Q once: wave w
+  // takes k-steps w, w+4, ..., the per-head maxima meet in LDS, the
+  // operands are staged in the V tile (untouched until the first tile's
+  // barrier) and every wave reads all 18 back.
   h16x8 qB[18];
   float qscale;          // |softmax_scale| * log2(e) * 2^p of head n
   {
+    constexpr int kQPer = (18 + kWaves - 1) / kWaves;   // k-steps per wave, at most
     const uint16_t* qrow = a.q + ((size_t)row * a.h_q + h0 + n) * kQkDim;
-    u32x4 raw[18];
+    u32x4 raw[kQPer];
 #pragma unroll
-    for (int ks = 0; ks < 16; ks++)
-      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * blk(g, ks >> 1) + 8 * (ks & 1));
-#pragma unroll
-    for (int ks = 16; ks < 18; ks++)
-      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
+    for (int i = 0; i < kQPer; i++) {
+      const int ks = wave + kWaves * i;                 // uniform over the wave
+      if (ks < 16)
+        raw[i] = *reinterpret_cast<const u32x4*>(qrow + 16 * blk(g, ks >> 1) + 8 * (ks & 1));
+      else if (ks < 18)
+        raw[i] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
+    }
     uint32_t am = 0;
 #pragma unroll
-    for (int ks = 0; ks < 18; ks++)
+    for (int i = 0; i < kQPer; i++)
+      if (wave + kWaves * i < 18)
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const uint32_t x = raw[ks][w];
-        am = max(am, max((x << 16) & 0x7FFFFFFFu, x & 0x7FFF0000u));
-      }
+        for (int w = 0; w < 4; w++) {
+          const uint32_t x = raw[i][w];
+          am = max(am, max((x << 16) & 0x7FFFFFFFu, x & 0x7FFF0000u));
+        }
     am = max(am, (uint32_t)__shfl_xor((int)am, 16));
     am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    // the loop's tile maxima reuse tmax only after the first tile's barrier
+    if (g == 0) tmax[wave][n] = __uint_as_float(am);
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) am = max(am, __float_as_uint(tmax[w][n]));
     // largest magnitude's exponent e: scale by 2^-(e-14) so it lands in [2^14, 2^15)
     int e = (int)(am >> 23) - 127;
     if (am == 0 || am >= 0x7F800000u) e = 14;
     const int p = max(e - 14, -100);
     const float mul = a.scale_log2 < 0.f ? -__builtin_ldexpf(1.0f, -p) : __builtin_ldexpf(1.0f, -p);
     qscale = fabsf(a.scale_log2) * __builtin_ldexpf(1.0f, p);
+    lds_b* const qst = (lds_b*)vtile;                   // [k-step][lane] x 16 bytes
 #pragma unroll
-    for (int ks = 0; ks < 18; ks++) {
+    for (int i = 0; i < kQPer; i++) {
+      const int ks = wave + kWaves * i;
+      if (ks >= 18) continue;
+      h16x8 v;
       if (F::kBf16Rope && ks >= 16) {
         // bf16 RoPE keys meet a bf16 Q operand (x * 2^-p is exact in bf16),
         // held in the same registers
-        bf16x8 v;
+        bf16x8 b;
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-          const uint32_t x = raw[ks][w];
-          v[2 * w] = (__bf16)(__uint_as_float(x << 16) * mul);
-          v[2 * w + 1] = (__bf16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+          const uint32_t x = raw[i][w];
+          b[2 * w] = (__bf16)(__uint_as_float(x << 16) * mul);
+          b[2 * w + 1] = (__bf16)(__uint_as_float(x & 0xFFFF0000u) * mul);
         }
-        qB[ks] = __builtin_bit_cast(h16x8, v);
+        v = __builtin_bit_cast(h16x8, b);
       } else {
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-          const uint32_t x = raw[ks][w];
-          qB[ks][2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
-          qB[ks][2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
+          const uint32_t x = raw[i][w];
+          v[2 * w] = (_Float16)(__uint_as_float(x << 16) * mul);
+          v[2 * w + 1] = (_Float16)(__uint_as_float(x & 0xFFFF0000u) * mul);
         }
       }
+      *reinterpret_cast<__attribute__((address_space(3))) h16x8*>(qst + (ks * 64 + lane) * 16) = v;
     }
+    lds_barrier();
+#pragma unroll
+    for (int ks = 0; ks < 18; ks++)
+      qB[ks] = *reinterpret_cast<const __attribute__((address_space(3))) h16x8*>(qst + (ks * 64 + lane) * 16);
   }
 
   f32x4 acc_o[8];
@@ -477,17 +498,31 @@ decode_tile16_kernel(DecodeArgs a) {
       denom += exp2f(a.sink[h0 + h] * kLog2e - tmax[0][h]);
     inv[r] = l > 0.f ? 1.0f / denom : 0.f;
   }
+  // Stage this wave's normalised block [16 heads][128 dv] in fp32 (rows
+  // padded to kStgRow floats: the 64 lanes of a column write hit 64 distinct
+  // banks) in the V tile, free since the first barrier above; it is
+  // wave-private, and a wave's LDS accesses complete in order.  Then each
+  // half-wave stores one head row of 128 dv: 4 values per lane.
+  constexpr int kStgRow = 132;
+  __attribute__((address_space(3))) float* const stg =
+      (__attribute__((address_space(3))) float*)(vtile + wave * (16 * kStgRow * 4));
 #pragma unroll
-  for (int nb = 0; nb < 8; nb++) {
-    const int dv = 128 * wave + 16 * nb + n;
+  for (int nb = 0; nb < 8; nb++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int h = 4 * g + r;
-      const float v = acc_o[nb][r] * inv[r];
-      if (a.splits == 1)
-        a.out[(orow + h) * kVDim + dv] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)v);
-      else
-        a.o_part[(prow + h) * kVDim + dv] = v;
+    for (int r = 0; r < 4; r++) stg[(4 * g + r) * kStgRow + 16 * nb + n] = acc_o[nb][r] * inv[r];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int h = 2 * i + (lane >> 5);
+    const int c = lane & 31;                     // dv 4c .. 4c+3 of this wave's 128
+    const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(stg + h * kStgRow + 4 * c);
+    const int dv = 128 * wave + 4 * c;
+    if (a.splits == 1) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const u32x2 b = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v.x, v.y}, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v.z, v.w}, bf16x2))};
+      *reinterpret_cast<u32x2*>(a.out + (orow + h) * kVDim + dv) = b;
+    } else {
+      *reinterpret_cast<f32x4*>(a.o_part + (prow + h) * kVDim + dv) = v;
     }
   }
   if (wave == 0 && g == 0) {

@@ -435,9 +435,12 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     for (int b = 0; b < 2; b++)
       *reinterpret_cast<lds_f32x4*>(xs + wave * kXsBytes + (b * 64 + lane) * 16) = sacc[b];
     // publish: the partial S (and every earlier LDS access of this wave)
-    // completes before the count moves
+    // completes before the count moves.  One lane stores it: 64 lanes
+    // storing to one LDS word conflict with each other, about 64 stall
+    // cycles per chunk.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __hip_atomic_store(flag + wave, (uint32_t)(pos + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0)
+      __hip_atomic_store(flag + wave, (uint32_t)(pos + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
   // wait until the partner has published chunk pos (bounded: the partner
   // runs the same number of chunks in the same workgroup)
