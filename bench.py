@@ -197,35 +197,55 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         ref.append(out.clone())
     # every call is capture-safe: capture each step's append and decode as HIP
     # graphs and check that replays reproduce the eager results bit for bit
-    g_app, g_dec = [], []
+    # one graph per step (append, then decode) for the step time; the append
+    # and decode on their own for the decode's event timing
+    g_app, g_dec, g_step = [], [], []
     if True:
         for r in range(nsets):
-            ga, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            ga, gd, gs = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
             with torch.cuda.graph(ga):
                 append(r)
             with torch.cuda.graph(gd):
                 decode(r)
+            with torch.cuda.graph(gs):
+                append(r)
+                decode(r)
             g_app.append(ga)
             g_dec.append(gd)
+            g_step.append(gs)
         for rnd in range(2):
             for r in range(nsets):
                 g_app[r].replay()
                 g_dec[r].replay()
                 torch.cuda.synchronize()
                 assert torch.equal(out, ref[r]), f"{name}: graph replay {rnd} set {r} differs"
+                g_step[r].replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out, ref[r]), f"{name}: step graph replay {rnd} set {r} differs"
     if time_graph:
         run_app = lambda r: g_app[r].replay()
         run_dec = lambda r: g_dec[r].replay()
+        run_step = lambda r: g_step[r].replay()
     else:
         run_app, run_dec = append, decode
 
+        def run_step(r):
+            append(r)
+            decode(r)
+
     for k in range(warmup):
-        run_app(k % nsets)
-        run_dec(k % nsets)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+        run_step(k % nsets)
+    # the step: wall time over `steps` back-to-back steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for k in range(steps):
+        run_step(k % nsets)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = (t1 - t0) * 1e3 / steps
+    # the decode alone: HIP events on the launching stream around each decode
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     for k in range(steps):
         r = k % nsets
         run_app(r)
@@ -233,10 +253,8 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         run_dec(r)
         ev[k][1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
     acc = decode_accounting(sets, wl)
-    step_ms = (t1 - t0) * 1e3 / steps
     dec_avg = float(dec_ms.mean())
     res = dict(
         workload=name, description=wl.description, rows=rows, h_q=wl.h_q, topk=wl.topk,
