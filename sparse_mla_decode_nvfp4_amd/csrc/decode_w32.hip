@@ -78,29 +78,32 @@ static_assert(32 * 4096 <= kOffStat, "merge slots overlap the statistics");
 // g): NoPE blocks s = 16hf + 4g + u (u = 0..3), 32 contiguous bytes; their
 // scales; RoPE dims 32hf + 8g .. +7.  In the 352-byte record block s's scale
 // sits at 320 + 8(s&3) + (s>>2), so the four are byte g of the dwords at
-// 320 + 8u + 4hf: the lane loads the whole 32-byte scale area (two wide
-// gathers rather than four narrow ones), and RoPE is 8 E4M3 bytes; in the
-// 432-byte record they are the four bytes of the dword at 256 + 16hf + 4g,
-// and RoPE is 8 bf16.
+// 320 + 8u + 4hf (two wide gathers cover them rather than four narrow ones),
+// and RoPE is 8 E4M3 bytes; in the 432-byte record they are the four bytes
+// of the dword at 256 + 16hf + 4g, and RoPE is 8 bf16.
 template <class F>
 struct RawP;
+// Scale dword 2u + hf of the 352-byte record's scale area holds blocks
+// 16hf + 4g + u (byte g).  A byte permute with selector byte 4hf + g picks
+// byte g of the first or second dword of a pair.
 template <>
 struct RawP<Fmt352> {
   u32x4 nope[2];
   u32x4 sc[2];           // the scale area: dword 2u + hf holds blocks 16hf + 4g + u
   u32x2 rope;
-  __device__ __forceinline__ uint32_t scale(int u, int g, int hf) const {
-    const u32x4& q = sc[u >> 1];
-    const uint32_t d = (u & 1) ? (hf ? q.w : q.z) : (hf ? q.y : q.x);
-    return (d >> (8 * g)) & 0xFFu;
+  // this lane's four scale bytes (block 16hf + 4g + u in byte u); sel[u]
+  // holds 4hf + g in byte u and 0x0c (a zero byte) elsewhere
+  __device__ __forceinline__ uint32_t scales(const uint32_t (&sel)[4]) const {
+    return (__builtin_amdgcn_perm(sc[0].y, sc[0].x, sel[0]) | __builtin_amdgcn_perm(sc[0].w, sc[0].z, sel[1])) |
+           (__builtin_amdgcn_perm(sc[1].y, sc[1].x, sel[2]) | __builtin_amdgcn_perm(sc[1].w, sc[1].z, sel[3]));
   }
 };
 template <>
 struct RawP<Fmt432> {
   u32x4 nope[2];
-  uint32_t sc;
+  uint32_t sc;           // block 16hf + 4g + u in byte u
   u32x4 rope;
-  __device__ __forceinline__ uint32_t scale(int u, int, int) const { return (sc >> (8 * u)) & 0xFFu; }
+  __device__ __forceinline__ uint32_t scales(const uint32_t (&)[4]) const { return sc; }
 };
 
 template <class F>
@@ -362,6 +365,13 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     }
   }
   const int partner = wave ^ 1;
+  // byte selectors of the 352-byte record's scales: byte u takes byte g of
+  // scale dword 2u + hf (selector 4hf + g over the dword pair), the others
+  // 0x0c (a zero byte)
+  uint32_t ssel[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+    ssel[u] = (0x0c0c0c0cu & ~(0xFFu << (8 * u))) | ((uint32_t)(4 * hf + g) << (8 * u));
 
   // Chunk pos from `cur` (cur_ok: whether this lane's token takes part), up to
   // the partial-S exchange; each raw piece is refilled with the next chunk's
@@ -378,12 +388,12 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     const uint8_t* const rec_next = rn.ptr;
     // block scales of this lane; zero for an invalid token, so its V row is
     // zero
+    const uint32_t sw = v ? cur.scales(ssel) : 0u;
     float S[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const uint32_t b = v ? cur.scale(u, g, hf) : 0u;
-      S[u] = __builtin_amdgcn_cvt_f32_fp8(b, 0);
-    }
+    S[0] = __builtin_amdgcn_cvt_f32_fp8(sw, 0);
+    S[1] = __builtin_amdgcn_cvt_f32_fp8(sw, 1);
+    S[2] = __builtin_amdgcn_cvt_f32_fp8(sw, 2);
+    S[3] = __builtin_amdgcn_cvt_f32_fp8(sw, 3);
     const auto rope = cur.rope;
     load_tail(cur, rec_next, hf, g);      // scales and RoPE of the next chunk
 #pragma unroll
