@@ -13,12 +13,12 @@
 //   * a workgroup owns one query row, one group of 16 heads and one split of
 //     the top-k list, and walks it in 64-token tiles; wave w loads and
 //     dequantizes tokens [16w, 16w+16) of each tile;
-//   * a lane loads the bytes of one token it needs straight from HBM (the
-//     permuted scale layout makes a lane's 8 block scales one 8-byte load)
-//     and dequantizes them to fp16 QK operands: every E2M1 x E4M3 product has
-//     at most 6 significant bits and lies in [2^-10, 2688], so it is exact in
-//     fp16 (the fp4 convert applies the scale's power of two, one packed
-//     multiply its mantissa); K never visits LDS, the NoPE half goes to the
+//   * a lane loads the bytes of one token it needs straight from HBM (64
+//     NoPE bytes, the scale area, 16 RoPE values) and dequantizes them to
+//     fp16 QK operands: every E2M1 x E4M3 product has at most 6 significant
+//     bits and lies in [2^-10, 2688], so it is exact in fp16 (the codes
+//     convert exactly, the scales convert exactly to fp16, one packed
+//     multiply gives the product); K never visits LDS, the NoPE half goes to the
 //     shared V tile (chunk-major: conflict-free row writes and transposed
 //     reads at immediate offsets);
 //   * Q is converted to fp16 once per wave with a per-head power-of-two scale
@@ -167,19 +167,16 @@ __device__ __forceinline__ void load_tok(RawTok<F>& t, const uint8_t* rec, int g
 }
 
 
-// Eight E2M1 codes times a block scale -> eight fp16, exact: the fp4 convert
-// applies the scale's power of two, F (the scale's mantissa as fp16) the rest.
-__device__ __forceinline__ h16x8 dequant8_f16(uint32_t w, float S, h16x2 F) {
-  const h16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 0) * F;
-  const h16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 1) * F;
-  const h16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 2) * F;
-  const h16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S, 3) * F;
+// Eight E2M1 codes times a block scale -> eight fp16, exact: the codes
+// convert exactly, the scale is an E4M3 value held exactly in fp16, and their
+// product has at most 6 significant bits in [2^-10, 2688].  F holds the
+// scale in both halves (a half-select of a packed pair of scales).
+__device__ __forceinline__ h16x8 dequant8_f16(uint32_t w, h16x2 F) {
+  const h16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * F;
+  const h16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * F;
+  const h16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * F;
+  const h16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * F;
   return h16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-__device__ __forceinline__ h16x2 mantissa_f16(float S) {
-  const float Fv = __uint_as_float((__float_as_uint(S) & 0x807FFFFFu) | 0x3F800000u);
-  return __builtin_bit_cast(h16x2, __builtin_amdgcn_cvt_pkrtz(Fv, Fv));   // exact: 4 bits
 }
 
 // Eight E4M3 RoPE bytes -> eight fp16 (exact).
@@ -375,18 +372,19 @@ decode_tile16_kernel(DecodeArgs a) {
     const u32x2 bsc = block_scales(cur, g);
     const uint32_t scx = cur_valid ? bsc.x : 0u;
     const uint32_t scy = cur_valid ? bsc.y : 0u;
-    const f32x2 s01 = e4m3x2_to_f32<0>(scx);
-    const f32x2 s23 = e4m3x2_to_f32<1>(scx);
-    const f32x2 s45 = e4m3x2_to_f32<0>(scy);
-    const f32x2 s67 = e4m3x2_to_f32<1>(scy);
-    const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
+    // the eight block scales as fp16 (exact), two per convert
+    const h16x2 sp[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scx, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scx, 1.0f, true),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scy, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scy, 1.0f, true)};
     f32x4 s_acc = {0.f, 0.f, 0.f, 0.f}, s_acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; c++) {
-      const h16x2 Fm = mantissa_f16(sc[c]);
+      const _Float16 sv = sp[c >> 1][c & 1];
+      const h16x2 Fs = {sv, sv};
 #pragma unroll
       for (int h = 0; h < 2; h++) {
-        const h16x8 k = dequant8_f16(nope_word(cur, c, h), sc[c], Fm);
+        const h16x8 k = dequant8_f16(nope_word(cur, c, h), Fs);
         *reinterpret_cast<__attribute__((address_space(3))) h16x8*>(
             (lds_b*)(size_t)vw_base + (2 * c + h) * kVChunk) = k;
         if (h == 0) s_acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qB[2 * c], s_acc, 0, 0, 0);

@@ -14,8 +14,8 @@
 //     registers, refilling each piece for the next chunk as soon as it has
 //     been used, and dequantizes them to fp16 MFMA operands: every E2M1 x
 //     E4M3 product has at most 6 significant bits and lies in [2^-10, 2688],
-//     so it is exact in fp16; the fp4 convert applies the scale's power of
-//     two, one packed multiply applies its mantissa;
+//     so it is exact in fp16: the codes convert exactly and one packed
+//     multiply by the scale (converted exactly to fp16) gives the product;
 //   * partial S^T = K Q^T (16 tokens x 32 heads: 16x16x32 MFMAs for two
 //     16-head blocks sharing each K operand) goes through LDS to the other
 //     half of the pair; both halves add the two partials (bit-identical sums)
@@ -389,11 +389,9 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     // block scales of this lane; zero for an invalid token, so its V row is
     // zero
     const uint32_t sw = v ? cur.scales(ssel) : 0u;
-    float S[4];
-    S[0] = __builtin_amdgcn_cvt_f32_fp8(sw, 0);
-    S[1] = __builtin_amdgcn_cvt_f32_fp8(sw, 1);
-    S[2] = __builtin_amdgcn_cvt_f32_fp8(sw, 2);
-    S[3] = __builtin_amdgcn_cvt_f32_fp8(sw, 3);
+    // the four block scales as fp16 (exact), two per convert
+    const f16x2 sp[2] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)};
     const auto rope = cur.rope;
     load_tail(cur, rec_next, hf, g);      // scales and RoPE of the next chunk
 #pragma unroll
@@ -401,13 +399,15 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       const int u = j >> 1;
-      const float Fv = __uint_as_float((__float_as_uint(S[u]) & 0x807FFFFFu) | 0x3F800000u);
-      const f16x2 Fm = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(Fv, Fv));   // exact
+      // codes convert exactly; times the fp16 scale (a half-select of its
+      // pair) the product is exact
+      const _Float16 sv = sp[u >> 1][u & 1];
+      const f16x2 Fs = {sv, sv};
       const uint32_t w = cur.nope[u >> 1][2 * (u & 1) + (j & 1)];
-      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 0) * Fm;
-      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 1) * Fm;
-      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 2) * Fm;
-      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, S[u], 3) * Fm;
+      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * Fs;
+      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * Fs;
+      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * Fs;
+      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * Fs;
       const f16x8 k = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
       *reinterpret_cast<lds_f16x8*>((lds_u8*)(size_t)wbase + (((8 * g + j) ^ vsw) << 4)) = k;
 #pragma unroll
