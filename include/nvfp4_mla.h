@@ -157,9 +157,10 @@ int nvfp4_mla_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row
 
 /*
  * Dequantize-gather: out[i, :] = the 576 bf16 values of the record at
- * slots[i] ([512 NoPE = e2m1 * scale | 64 RoPE]), exactly as the decode
- * dequantizes them (every value is exact in bf16).  slots[i] < 0 or beyond
- * the cache gives a row of zeros.
+ * slots[i] ([512 NoPE = e2m1 * scale | 64 RoPE]): the values the decode
+ * uses as its K and V operands, which are exact there (in fp16) and here (in
+ * bf16), so both hold the same numbers.  slots[i] < 0 or beyond the cache
+ * gives a row of zeros.
  *   slots   [n] int32;  out_bf16 [n, 576] bf16 contiguous.
  */
 int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks,
