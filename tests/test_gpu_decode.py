@@ -4,7 +4,8 @@ rows exact.  Small cases span several 16-token blocks, several head groups,
 ragged tails, splits, invalid and out-of-range indices; the four decode
 workloads run at full size with the planner's split choice (the launch
 configuration the benchmark times) and are compared on sampled rows, with
-every row checked for finite values.
+every row checked for finite values.  Rows with a single valid token pin the
+decode's own dequant bit for bit over every (code, scale) product.
 """
 
 import numpy as np
@@ -206,3 +207,53 @@ def test_workspace_reuse_and_garbage_workspace(lib):
             assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
         _, _, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
         assert_decode_close(outs[0][0], outs[0][1], o_ref, l_ref, f"reused workspace h{h}")
+
+
+def crafted_code_scale_records(record_bytes, seed=5):
+    """127 records that together hold every E2M1 code under every finite E4M3
+    scale byte (0 and the subnormals included): record r gives block s the
+    scale byte (r + 5s) mod 127 and element i the code (i + r) mod 16, so
+    each block holds all 16 codes.  RoPE bytes are small finite values."""
+    rng = np.random.default_rng(seed)
+    n = 127
+    rec = np.zeros((n, record_bytes), np.uint8)
+    i = np.arange(512)
+    for r in range(n):
+        codes = (i + r) % 16
+        rec[r, :256] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+        rec[r, OC._scale_positions(record_bytes)] = (r + 5 * np.arange(32)) % 127
+    if record_bytes == 352:
+        # E4M3 bytes with exponent field <= 9: |value| < 8
+        rec[:, 256:320] = (rng.integers(0, 80, (n, 64)) | (rng.integers(0, 2, (n, 64)) << 7)).astype(np.uint8)
+    else:
+        rope = rng.standard_normal((n, 64)).astype(np.float32)
+        rec[:, 304:432] = (rope.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(n, 128)
+    return rec
+
+
+@pytest.mark.parametrize("h,splits,rb", [(16, 1, 352), (32, 1, 352), (64, 3, 352), (128, 1, 352),
+                                         (16, 2, 432), (64, 1, 432)])
+def test_single_valid_token_returns_every_code_scale_product_exactly(lib, h, splits, rb):
+    # each row has one valid token among invalid ones, so its weight is 1 and
+    # O is that record's dequantized NoPE row, bit for bit in bf16; the
+    # records cover all 16 x 127 (code, scale) products
+    note(f"code x scale through the decode h={h} splits={splits} record={rb}")
+    recs = crafted_code_scale_records(rb)
+    n = recs.shape[0]
+    bs = 64
+    nb = -(-n // bs)
+    full = np.zeros((nb * bs, rb), np.uint8)
+    full[:n] = recs
+    rng = np.random.default_rng(h + splits)
+    topk = 37
+    idx = np.full((n, 1, topk), -1, np.int32)
+    idx[np.arange(n), 0, rng.integers(0, topk, n)] = np.arange(n)
+    q = torch.from_numpy(rng.standard_normal((n, 1, h, 576)).astype(np.float32)).to(torch.bfloat16)
+    cache = torch.from_numpy(full.reshape(nb, bs, rb)).to(DEV)
+    o, lse = lib.sparse_decode(q.to(DEV), cache, torch.from_numpy(idx).to(DEV), 1.0 / 24,
+                               num_splits=splits)
+    torch.cuda.synchronize()
+    v = torch.from_numpy(OC.dequantize_records(recs)[:, :512]).to(torch.bfloat16)
+    assert torch.equal(o[:, 0].cpu(), v[:, None, :].expand(n, h, 512))
+    o_ref, l_ref = OA.sparse_decode(f64(q), recs, idx, 1.0 / 24)
+    assert_decode_close(o, lse, o_ref, l_ref, f"code x scale h={h}")
