@@ -307,6 +307,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   a.out = static_cast<uint16_t*>(out_bf16);
   a.lse = lse;
   a.splits = splits;
+  a.num_cus = cus;
   if (splits > 1) {
     const WsLayout w = ws_layout(rows, h_q, splits);
     char* base = static_cast<char*>(workspace);

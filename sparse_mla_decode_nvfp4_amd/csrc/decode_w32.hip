@@ -54,7 +54,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
-constexpr int kWavesP = 8;
 constexpr int kChunkP = 16;                        // tokens per chunk
 constexpr int kVRowP = 256 * 2;                    // fp16 V half-row
 constexpr int kVTileP = kChunkP * kVRowP;          // 8 KB per wave
@@ -64,15 +63,27 @@ constexpr float kLazyP = 15.0f;                    // P = 2^(s - m_run) <= 2^15
 constexpr float kLn2P = 0.6931471805599453f;
 constexpr float kLog2eP = 1.4426950408889634f;
 
-// LDS map (bytes): V tiles, partial-S exchange (double-buffered), Q
-// operands, then per-head statistics; the first 128 KB are reused for the
-// final merge of the pairs.
-constexpr int kOffXs = kWavesP * kVTileP;                  // 64 KB
-constexpr int kOffQ = kOffXs + 2 * kWavesP * kXsBytes;     // 96 KB
-constexpr int kOffStat = kOffQ + kQBytes;                  // 132 KB
-constexpr int kOffFlag = kOffStat + kWavesP * 2 * 32 * 4 + 2 * 32 * 4;
-constexpr int kLdsBytes = kOffFlag + kWavesP * 4;
-static_assert(32 * 4096 <= kOffStat, "merge slots overlap the statistics");
+// LDS map (bytes) of a workgroup of kPairs pairs: V tiles, partial-S
+// exchange, Q operands, per-head statistics, then the pair counters.  Four
+// pairs (one workgroup per CU) double-buffer the exchange; two pairs keep one
+// exchange buffer per wave so that two workgroups fit in a CU's 160 KB.  The
+// merge of the pairs at the end reuses the space below the statistics.
+template <int kPairs>
+struct LdsW32 {
+  static constexpr int kWaves = 2 * kPairs;
+  static constexpr int kXsBufs = kPairs == 4 ? 2 : 1;
+  static constexpr int kOffXs = kWaves * kVTileP;
+  static constexpr int kOffQ = kOffXs + kXsBufs * kWaves * kXsBytes;
+  static constexpr int kOffStat = kOffQ + kQBytes;
+  static constexpr int kOffFlag = kOffStat + kWaves * 2 * 32 * 4 + 2 * 32 * 4;
+  static constexpr int kBytes = kOffFlag + 2 * kWaves * 4;     // published, consumed
+  // merge: 4 slots of 4 KB per wave in round one, then an 8 KB output
+  // stage per wave (past the round-two slots for four pairs, from 0 for two)
+  static constexpr int kOffStage = kPairs == 4 ? 16 * 4096 : 0;
+  static_assert(4 * kWaves * 4096 <= kOffStat, "merge slots overlap the statistics");
+  static_assert(kOffStage + kWaves * 8192 <= kOffStat, "output stage overlaps the statistics");
+};
+static_assert(LdsW32<2>::kBytes <= 80 * 1024, "two workgroups of two pairs must fit in a CU");
 
 // This lane's share of one record (token n of the chunk, half hf, lane group
 // g): NoPE blocks s = 16hf + 4g + u (u = 0..3), 32 contiguous bytes; their
@@ -188,15 +199,18 @@ struct IntC {
 //   C = S^T[token 4g+r][head 16b+n] for head blocks b = 0, 1.
 //   PV (32x32x16): A = P[head tl][token 8kg+i], B = V[token 8kg+i][dv 32nb +
 //   tl], C = O[head acc_row(r, kg)][dv 256hf + 32nb + tl].
-template <bool kDual, class F>
-__global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs a) {
+template <bool kDual, class F, int kPairs>
+__global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_kernel(DecodeArgs a) {
+  using L = LdsW32<kPairs>;
+  constexpr int kWavesP = L::kWaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_p[];
   lds_u8* const lds = (lds_u8*)smem_p;
-  lds_u8* const xs_all = lds + kOffXs;
-  lds_u8* const qlds = lds + kOffQ;
-  lds_f32* const stat = (lds_f32*)(lds + kOffStat);                          // [wave][m, l][32]
-  lds_u32* const qmax = (lds_u32*)(lds + kOffStat + kWavesP * 2 * 32 * 4);   // [half][32]
-  lds_u32* const flag = (lds_u32*)(lds + kOffFlag);   // [wave]: chunks whose partial S is published
+  lds_u8* const xs_all = lds + L::kOffXs;
+  lds_u8* const qlds = lds + L::kOffQ;
+  lds_f32* const stat = (lds_f32*)(lds + L::kOffStat);                        // [wave][m, l][32]
+  lds_u32* const qmax = (lds_u32*)(lds + L::kOffStat + kWavesP * 2 * 32 * 4); // [half][32]
+  lds_u32* const flag = (lds_u32*)(lds + L::kOffFlag);   // [wave]: chunks whose partial S is published
+  lds_u32* const consumed = flag + kWavesP;              // [wave]: partner chunks read (one buffer)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -243,10 +257,12 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   // 3 take 4 (p, p+4, p+8, p+12).  Pairs 0 and 1 are the first waves of their
   // SIMDs, which issue first and run about 1.25 times as fast, so the pairs
   // finish together; the fixed deal keeps the summation order, and so the
-  // result, the same on every run.  cid0..cid2 are this pair's chunks pos,
-  // pos+1 and pos+2.
+  // result, the same on every run.  With two pairs (both the first, or both
+  // the second, waves of their SIMDs) the chunks alternate.  cid0..cid2 are
+  // this pair's chunks pos, pos+1 and pos+2.
   const int kp = pr < 2 ? 5 : 4;
   auto cid_of = [&](int i) {
+    if constexpr (kPairs == 2) return pr + 2 * i;
     const int blk = i / kp, j = i - blk * kp;
     return 18 * blk + (j < 4 ? pr + 4 * j : 16 + pr);
   };
@@ -298,7 +314,10 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
       amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32));
       if (g == 0) qmax[hf * 32 + 16 * pr + n] = amax_bits;
     }
-    if (lane == 0) flag[wave] = 0;
+    if (lane == 0) {
+      flag[wave] = 0;
+      consumed[wave] = 0;
+    }
     lds_sync_p();
     int pq[2];
 #pragma unroll
@@ -440,7 +459,16 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     }
     cur_ok = rn.ok;
     nxt_raw = nxt2_raw;
-    lds_u8* const xs = xs_all + (pos & 1) * kWavesP * kXsBytes;
+    lds_u8* const xs = xs_all + (L::kXsBufs == 2 ? (pos & 1) : 0) * kWavesP * kXsBytes;
+    if constexpr (L::kXsBufs == 1) {
+      // one buffer: the partner must have read this wave's previous chunk
+      // (bounded: it reads it right after its own exchange write)
+      for (int it = 0; it < (1 << 22); it++) {
+        if ((int)__hip_atomic_load(consumed + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= pos) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
 #pragma unroll
     for (int b = 0; b < 2; b++)
       *reinterpret_cast<lds_f32x4*>(xs + wave * kXsBytes + (b * 64 + lane) * 16) = sacc[b];
@@ -464,13 +492,19 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
 
   // After the exchange: full S^T, online softmax, O += P V.
   auto post = [&](int pos) {
-    lds_u8* const xs = xs_all + (pos & 1) * kWavesP * kXsBytes;
+    lds_u8* const xs = xs_all + (L::kXsBufs == 2 ? (pos & 1) : 0) * kWavesP * kXsBytes;
     float s[2][4];
 #pragma unroll
     for (int b = 0; b < 2; b++) {
       const f32x4 o4 = *reinterpret_cast<const lds_f32x4*>(xs + partner * kXsBytes + (b * 64 + lane) * 16);
 #pragma unroll
       for (int r = 0; r < 4; r++) s[b][r] = sacc[b][r] + o4[r];
+    }
+    if constexpr (L::kXsBufs == 1) {
+      // the partner's partial S is read: it may write its next one
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0)
+        __hip_atomic_store(consumed + wave, (uint32_t)(pos + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     // lane holds heads n, 16+n and tokens 4g+r; invalid tokens -> -inf
     // (a per-lane select on okbits: no scalar mask building)
@@ -585,10 +619,10 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   for (int b = 0; b < 2; b++) {
     float M = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < 4; p++) M = fmaxf(M, stat[((2 * p + hf) * 2) * 32 + 16 * b + n]);
+    for (int p = 0; p < kPairs; p++) M = fmaxf(M, stat[((2 * p + hf) * 2) * 32 + 16 * b + n]);
     float L = 0.f;
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
+    for (int p = 0; p < kPairs; p++) {
       const float mp = stat[((2 * p + hf) * 2) * 32 + 16 * b + n];
       if (mp != -INFINITY) L += stat[((2 * p + hf) * 2 + 1) * 32 + 16 * b + n] * __builtin_amdgcn_exp2f(mp - M);
     }
@@ -666,11 +700,14 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
     for (int u = 0; u < 2; u++) add(2 * (wave ^ 4) + u, acc_o[kKeep + u]);
   };
   // blocks owned at the end: pair 0: 0,1; pair 1: 4,5; pair 2: 2,3; pair 3: 6,7
-  switch (pr) {
-    case 0: round2(IntC<0>{}, IntC<2>{}); break;
-    case 1: round2(IntC<4>{}, IntC<6>{}); break;
-    case 2: round2(IntC<2>{}, IntC<0>{}); break;
-    default: round2(IntC<6>{}, IntC<4>{}); break;
+  // (two pairs: pair 0 keeps 0..3 and pair 1 4..7 after round 1)
+  if constexpr (kPairs == 4) {
+    switch (pr) {
+      case 0: round2(IntC<0>{}, IntC<2>{}); break;
+      case 1: round2(IntC<4>{}, IntC<6>{}); break;
+      case 2: round2(IntC<2>{}, IntC<0>{}); break;
+      default: round2(IntC<6>{}, IntC<4>{}); break;
+    }
   }
 
   // ---- normalise and write this wave's two output blocks
@@ -693,11 +730,12 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   }
   const size_t orow = (size_t)row * a.h_q + h0;
   const size_t prow = ((size_t)split * a.rows + row) * a.h_q + h0;
-  // Stage this wave's two blocks as [32 heads][64 dv] fp32 (free space past
-  // the round-2 slots), then store rows of 8 dv per lane.  Column c of head
-  // row h sits at c ^ 32((h>>2)&1) ^ 4(h&1): the two lane halves of a write
-  // (heads 4 apart) and neighbouring heads of a read use disjoint banks.
-  lds_f32* const stg = (lds_f32*)(lds + 16 * 4096 + wave * 8192);
+  // Stage two of this wave's blocks at a time as [32 heads][64 dv] fp32
+  // (wave-private space past the merge slots still in use), then store rows
+  // of 8 dv per lane.  Column c of head row h sits at c ^ 32((h>>2)&1) ^
+  // 4(h&1): the two lane halves of a write (heads 4 apart) and neighbouring
+  // heads of a read use disjoint banks.
+  lds_f32* const stg = (lds_f32*)(lds + L::kOffStage + wave * 8192);
   auto stage_blocks = [&](auto base_c) {
     constexpr int kB = decltype(base_c)::value;
 #pragma unroll
@@ -708,14 +746,7 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
         stg[hr * 64 + ((((u ^ kg) << 5) | tl) ^ ((r & 1) << 2))] = acc_o[kB + u][r] * inv[r];
       }
   };
-  int kb;
-  switch (pr) {
-    case 0: stage_blocks(IntC<0>{}); kb = 0; break;
-    case 1: stage_blocks(IntC<4>{}); kb = 4; break;
-    case 2: stage_blocks(IntC<2>{}); kb = 2; break;
-    default: stage_blocks(IntC<6>{}); kb = 6; break;
-  }
-  {
+  auto store_blocks = [&](int kb) {
     const int ch = lane & 7;                  // 8-dv chunk of the 64 staged dv
     const int dv0 = 256 * hf + 32 * kb + 8 * ch;
 #pragma unroll
@@ -741,6 +772,26 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
         *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o_part) + (prow + h) * kVDim + dv0) = v;
       }
     }
+  };
+  if constexpr (kPairs == 4) {
+    int kb;
+    switch (pr) {
+      case 0: stage_blocks(IntC<0>{}); kb = 0; break;
+      case 1: stage_blocks(IntC<4>{}); kb = 4; break;
+      case 2: stage_blocks(IntC<2>{}); kb = 2; break;
+      default: stage_blocks(IntC<6>{}); kb = 6; break;
+    }
+    store_blocks(kb);
+  } else if (pr == 0) {
+    stage_blocks(IntC<0>{});
+    store_blocks(0);
+    stage_blocks(IntC<2>{});
+    store_blocks(2);
+  } else {
+    stage_blocks(IntC<4>{});
+    store_blocks(4);
+    stage_blocks(IntC<6>{});
+    store_blocks(6);
   }
   if (wave == 0 && g == 0) {
 #pragma unroll
@@ -752,29 +803,37 @@ __global__ void __launch_bounds__(64 * kWavesP, 1) decode_w32_kernel(DecodeArgs 
   }
 }
 
-size_t decode_w32_lds_bytes() { return kLdsBytes; }
-
-template <bool kDual, class F>
-static hipError_t launch_w32_kernel(const DecodeArgs& a, int grid, size_t lds, hipStream_t stream) {
+template <bool kDual, class F, int kPairs>
+static hipError_t launch_w32_kernel(const DecodeArgs& a, int grid, hipStream_t stream) {
+  constexpr size_t lds = LdsW32<kPairs>::kBytes;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel<kDual, F>,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel<kDual, F, kPairs>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((decode_w32_kernel<kDual, F>), dim3(grid), dim3(64 * kWavesP), lds, stream, a);
+  hipLaunchKernelGGL((decode_w32_kernel<kDual, F, kPairs>), dim3(grid), dim3(128 * kPairs), lds, stream, a);
   return hipSuccess;
+}
+
+template <bool kDual, class F>
+static hipError_t launch_w32_pairs(const DecodeArgs& a, int grid, hipStream_t stream) {
+  // Four pairs per workgroup (one per CU) when the launch is at most a few
+  // workgroups per CU.  With many (a prefill), two pairs per workgroup and
+  // two workgroups per CU: one workgroup's set-up and final merge then run
+  // beside the other's chunk loop.
+  if ((int64_t)grid >= 4 * (int64_t)a.num_cus) return launch_w32_kernel<kDual, F, 2>(a, grid, stream);
+  return launch_w32_kernel<kDual, F, 4>(a, grid, stream);
 }
 
 hipError_t launch_decode_w32(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.rows * (a.h_q / 32) * a.splits;
-  const size_t lds = decode_w32_lds_bytes();
   const bool f432 = a.pa.record_bytes == Fmt432::kBytes;
-  hipError_t e0 = a.cache1 ? (f432 ? launch_w32_kernel<true, Fmt432>(a, grid, lds, stream)
-                                   : launch_w32_kernel<true, Fmt352>(a, grid, lds, stream))
-                           : (f432 ? launch_w32_kernel<false, Fmt432>(a, grid, lds, stream)
-                                   : launch_w32_kernel<false, Fmt352>(a, grid, lds, stream));
+  hipError_t e0 = a.cache1 ? (f432 ? launch_w32_pairs<true, Fmt432>(a, grid, stream)
+                                   : launch_w32_pairs<true, Fmt352>(a, grid, stream))
+                           : (f432 ? launch_w32_pairs<false, Fmt432>(a, grid, stream)
+                                   : launch_w32_pairs<false, Fmt352>(a, grid, stream));
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;

@@ -46,6 +46,7 @@ struct DecodeArgs {
                             // in its first half from the 32-head kernel
   float* lse_part;          // [splits, rows, h_q]
   int32_t splits;
+  int32_t num_cus;          // compute units of the device (picks the 32-head kernel's shape)
 };
 
 // Decode launch: head counts that are multiples of 32 run the 32-head-group

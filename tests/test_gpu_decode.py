@@ -257,3 +257,20 @@ def test_single_valid_token_returns_every_code_scale_product_exactly(lib, h, spl
     assert torch.equal(o[:, 0].cpu(), v[:, None, :].expand(n, h, 512))
     o_ref, l_ref = OA.sparse_decode(f64(q), recs, idx, 1.0 / 24)
     assert_decode_close(o, lse, o_ref, l_ref, f"code x scale h={h}")
+
+
+# Launches of at least four workgroups per CU (a prefill's many query rows)
+# run the 32-head kernel with two pairs per workgroup, two workgroups per CU.
+# These cases are large enough to take that path (>= 1024 workgroups on 256
+# CUs) and small enough to check every row: odd chunk counts give the two
+# pairs different numbers of chunks.
+@pytest.mark.parametrize("b,h,topk,splits,p_inval", [
+    (512, 64, 100, 1, 0.1), (256, 128, 77, 1, 0.3), (512, 32, 300, 2, 0.05), (1024, 32, 33, 1, 0.5),
+])
+def test_many_workgroups_every_row(lib, b, h, topk, splits, p_inval):
+    note(f"many workgroups b={b} h={h} topk={topk} splits={splits}")
+    recs, q, idx, sink, nb, bs = small_case(41 + h, b, 1, h, topk, nblocks=40, p_inval=p_inval, dup=True)
+    idx[3, 0, :] = -1                       # an empty row
+    o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
+    assert_decode_close(o, lse, o_ref, l_ref, f"many workgroups h={h} splits={splits}")
+    assert bool((o[3].cpu() == 0).all()) and bool(torch.isneginf(lse[3]).all())

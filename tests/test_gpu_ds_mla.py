@@ -147,3 +147,23 @@ def test_ds_mla_dual_cache_decode(lib, h):
     o_ref, l_ref = OA.sparse_decode_dual(f64(q), r0, i0, r1, i1, 1.0 / 24,
                                          sink=sink.astype(np.float64))
     assert_decode_close(o, lse, o_ref, l_ref, f"432-byte dual h{h}")
+
+
+def test_ds_mla_many_workgroups_every_row(lib):
+    # >= 1024 workgroups: the 32-head kernel's two-pair shape on 432-byte records
+    note("ds_mla many workgroups")
+    h, b, topk = 64, 512, 90
+    rng = np.random.default_rng(77)
+    n = 40 * 64
+    lat, rope = W.latents(0, n, rep=77)
+    recs = OC.quantize_records(f64(lat), f64(rope), 432)
+    q = torch.from_numpy(rng.standard_normal((b, 1, h, 576)).astype(np.float32)).to(torch.bfloat16)
+    idx = rng.integers(0, n, size=(b, 1, topk)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    sink = rng.standard_normal(h).astype(np.float32)
+    cache = torch.from_numpy(recs.reshape(40, 64, 432)).to(DEV)
+    o, lse = lib.sparse_decode(q.to(DEV), cache, torch.from_numpy(idx).to(DEV), 1.0 / 24,
+                               sink=torch.from_numpy(sink).to(DEV), num_splits=1)
+    torch.cuda.synchronize()
+    o_ref, l_ref = OA.sparse_decode(f64(q), recs, idx, 1.0 / 24, sink=sink.astype(np.float64))
+    assert_decode_close(o, lse, o_ref, l_ref, "ds_mla many workgroups")

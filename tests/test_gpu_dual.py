@@ -155,3 +155,11 @@ def test_dual_full_size_mtp_workload(lib):
     note(f"{wl.name}: splits={splits}, worst error/bound over {len(sample)} rows = {worst:.3f}")
     del c0, c1
     torch.cuda.empty_cache()
+
+
+def test_dual_many_workgroups_every_row(lib):
+    # >= 1024 workgroups: the 32-head kernel's two-pair shape over two caches
+    note("dual many workgroups")
+    case = dual_case(91, 512, 1, 64, 64, 100, 64, 8, 2, 300)
+    o, lse, o_ref, l_ref = run_dual(lib, case, 64, 2, 1)
+    assert_decode_close(o, lse, o_ref, l_ref, "dual many workgroups")
