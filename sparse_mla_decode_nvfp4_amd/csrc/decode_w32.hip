@@ -6,8 +6,10 @@
 // optional per-head sink, O = P V over 512 dims.  Organisation:
 //
 //   * a workgroup of eight waves (two per SIMD) owns one (query row, 32-head
-//     group, split).  Waves 2p and 2p+1 form pair p (p = 0..3); pair p takes
-//     every fourth 16-token chunk of the split.  Within a pair, wave half hf
+//     group, split).  Waves 2p and 2p+1 form pair p (p = 0..3); the pairs
+//     share out the split's 16-token chunks.  Launches of many workgroups
+//     per CU use workgroups of two pairs instead, two per CU, so that one
+//     workgroup's set-up and merge overlap the other's chunks.  Within a pair, wave half hf
 //     owns NoPE blocks 16hf..16hf+15 plus RoPE dims 32hf..32hf+31 of the QK
 //     contraction (288 dims) and output dims 256hf..256hf+255 of O;
 //   * a wave gathers its half of each chunk's records straight into
@@ -29,8 +31,9 @@
 //   * P is rounded to fp16 for the PV product (relative error 2^-12); the
 //     running max is raised lazily, only when a score exceeds it by more than
 //     2^15 (P stays in fp16 range and rescales of O are rare);
-//   * the four pairs merge their states through LDS at the end (two rounds of
-//     pairwise sums), and each wave writes an eighth of the output dims.
+//   * the pairs merge their states through LDS at the end (pairwise sums: two
+//     rounds for four pairs, one for two), and each wave writes its share of
+//     the output dims.
 // Split partials (sink-free O normalised within the split, in fp16, and LSE)
 // are merged by the combine kernel launched right after; all workgroups of a row share an
 // XCD when the row count allows (the row's records stay in that XCD's L2).
