@@ -28,13 +28,35 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_mag(float q) {
 }
 
 // Magnitude code (0..7) of |x| on the E2M1 grid {0,.5,1,1.5,2,3,4,6} * s,
-// ties to the even code.  Thresholds s*{.25,.75,1.25,1.75,2.5,3.5,5} are exact
-// fp32 products; a tie rounds toward the even code, hence > vs >=.
-__device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
-  uint32_t c = (a > 0.25f * s) + (a >= 0.75f * s) + (a > 1.25f * s) +
-               (a >= 1.75f * s) + (a > 2.5f * s) + (a >= 3.5f * s) + (a > 5.0f * s);
-  return s == 0.0f ? 0u : c;
-}
+// ties to the even code.  The thresholds t_k = s*{.25,.75,1.25,1.75,2.5,3.5,5}
+// between codes k and k+1 are exact fp32 products; a tie at t_k goes to the
+// even one of k and k+1, hence >= for odd k and > for even k.  The code is
+// found bit by bit: bit 2 from t_3, bit 1 from t_1 or t_5, bit 0 from
+// t_0, t_2, t_4 or t_6.  A zero scale gives infinite thresholds (code 0).
+struct E2m1Thresholds {
+  float t[7];
+  __device__ __forceinline__ explicit E2m1Thresholds(float s) {
+    const float inf = __builtin_inff();
+    t[0] = s == 0.0f ? inf : 0.25f * s;
+    t[1] = s == 0.0f ? inf : 0.75f * s;
+    t[2] = s == 0.0f ? inf : 1.25f * s;
+    t[3] = s == 0.0f ? inf : 1.75f * s;
+    t[4] = s == 0.0f ? inf : 2.5f * s;
+    t[5] = s == 0.0f ? inf : 3.5f * s;
+    t[6] = s == 0.0f ? inf : 5.0f * s;
+  }
+  // the selects are written as bit masks so that they stay selects
+  __device__ __forceinline__ static float pick(uint32_t m, float x, float y) {   // m ? x : y
+    return __uint_as_float((__float_as_uint(x) & m) | (__float_as_uint(y) & ~m));
+  }
+  __device__ __forceinline__ uint32_t code(float a) const {
+    const uint32_t m2 = 0u - (uint32_t)(a >= t[3]);
+    const uint32_t m1 = 0u - (uint32_t)(a >= pick(m2, t[5], t[1]));
+    const float tl = pick(m2, pick(m1, t[6], t[4]), pick(m1, t[2], t[0]));
+    const uint32_t b0 = (uint32_t)(a > tl);
+    return (m2 & 4u) | (m1 & 2u) | b0;
+  }
+};
 
 // A 16-bit input element (bf16, or fp16 when kF16) widened to fp32, exactly.
 template <bool kF16>
@@ -43,11 +65,13 @@ __device__ __forceinline__ float widen16(uint32_t bits16) {
   else return __uint_as_float(bits16 << 16);
 }
 
-// One wavefront per token; 4 tokens per 256-thread block.  Lane l quantizes
-// NoPE elements [8l, 8l+8) (block l/2) and RoPE element l; the record is
-// assembled in LDS and written with 16-byte stores (22 or 27).  The input is
-// bf16, or fp16 when kF16 (352-byte record only): every fp16 or bf16 value is
-// exact in fp32, so the rounding below is the same for both.
+// One wavefront per kTokW consecutive tokens; 4 waves per 256-thread block.
+// Lane l quantizes NoPE elements [8l, 8l+8) (block l/2) and RoPE element l;
+// each record is assembled in LDS and written with 16-byte stores (22 or 27).
+// The input is bf16, or fp16 when kF16 (352-byte record only): every fp16 or
+// bf16 value is exact in fp32, so the rounding below is the same for both.
+constexpr int kTokW = 4;
+
 template <bool kF16, class F>
 __global__ void __launch_bounds__(256)
 quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
@@ -58,49 +82,63 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
   __shared__ __attribute__((aligned(16))) uint8_t rec[4][F::kBytes];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
-  if (tok >= num_tokens) return;
-  const int64_t slot = slot_mapping[tok];
-  if (slot < 0 || slot >= num_slots) return;          // wave-uniform skip
-
+  const int64_t tok0 = ((int64_t)blockIdx.x * 4 + wave) * kTokW;
+  if (tok0 >= num_tokens) return;
+  // every token's slot, latent and RoPE are requested up front (one memory
+  // round trip for the wave's tokens); a skipped token's record is built too
+  // and only its store is dropped
+  int64_t slot[kTokW];
+  u32x4 raw[kTokW];
+  uint32_t rbits[kTokW];
+#pragma unroll
+  for (int t = 0; t < kTokW; t++) {
+    const int64_t tok = min(tok0 + t, num_tokens - 1);
+    slot[t] = tok0 + t < num_tokens ? slot_mapping[tok] : -1;
+    raw[t] = *reinterpret_cast<const u32x4*>(latent + tok * lstride + 8 * lane);
+    rbits[t] = (uint32_t)rope[tok * rstride + lane];
+  }
   uint8_t* r = rec[wave];
-  // ---- NoPE: 8 elements per lane, two lanes per 16-element block
-  const u32x4 raw = *reinterpret_cast<const u32x4*>(latent + tok * lstride + 8 * lane);
-  float x[8];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    x[2 * i] = widen16<kF16>(raw[i] & 0xFFFFu);
-    x[2 * i + 1] = widen16<kF16>(raw[i] >> 16);
-  }
-  float amax = 0.0f;
+  for (int t = 0; t < kTokW; t++) {
+    const bool mapped = slot[t] >= 0 && slot[t] < num_slots;   // uniform over the wave
+    // ---- NoPE: 8 elements per lane, two lanes per 16-element block
+    float x[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  const uint32_t scode = e4m3_rne_sat_mag(__fdiv_rn(amax, 6.0f));
-  const float sv = e4m3x2_to_f32<0>(scode).x;
-  uint32_t packed = 0;
+    for (int i = 0; i < 4; i++) {
+      x[2 * i] = widen16<kF16>(raw[t][i] & 0xFFFFu);
+      x[2 * i + 1] = widen16<kF16>(raw[t][i] >> 16);
+    }
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint32_t code = e2m1_mag(fabsf(x[i]), sv) | ((__float_as_uint(x[i]) >> 28) & 8u);
-    packed |= code << (4 * i);
-  }
-  reinterpret_cast<uint32_t*>(r)[lane] = packed;
-  if ((lane & 1) == 0) r[F::scale_at(lane >> 1)] = (uint8_t)scode;
-  // ---- RoPE: lane l handles element l
-  const uint32_t rbits = (uint32_t)rope[tok * rstride + lane];
-  if constexpr (F::kBf16Rope) {
-    reinterpret_cast<uint16_t*>(r + F::kRopeOff)[lane] = (uint16_t)rbits;   // verbatim
-    if (lane < 4) reinterpret_cast<uint32_t*>(r + F::kPadOff)[lane] = 0u;
-  } else {
-    const float rv = widen16<kF16>(rbits);
-    const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
-    r[F::kRopeOff + lane] = (uint8_t)rcode;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  if (lane < F::kBytes / 16) {
-    uint8_t* dst = cache + pa.offset((uint32_t)slot);
-    reinterpret_cast<u32x4*>(dst)[lane] = reinterpret_cast<const u32x4*>(r)[lane];
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    const uint32_t scode = e4m3_rne_sat_mag(__fdiv_rn(amax, 6.0f));
+    const E2m1Thresholds th(e4m3x2_to_f32<0>(scode).x);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      uint32_t code = th.code(fabsf(x[i])) | ((__float_as_uint(x[i]) >> 28) & 8u);
+      packed |= code << (4 * i);
+    }
+    // the previous token's record has been read out of the staging area
+    __builtin_amdgcn_wave_barrier();
+    reinterpret_cast<uint32_t*>(r)[lane] = packed;
+    if ((lane & 1) == 0) r[F::scale_at(lane >> 1)] = (uint8_t)scode;
+    // ---- RoPE: lane l handles element l
+    if constexpr (F::kBf16Rope) {
+      reinterpret_cast<uint16_t*>(r + F::kRopeOff)[lane] = (uint16_t)rbits[t];   // verbatim
+      if (lane < 4) reinterpret_cast<uint32_t*>(r + F::kPadOff)[lane] = 0u;
+    } else {
+      const float rv = widen16<kF16>(rbits[t]);
+      const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
+      r[F::kRopeOff + lane] = (uint8_t)rcode;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    if (mapped && lane < F::kBytes / 16) {
+      uint8_t* dst = cache + pa.offset((uint32_t)slot[t]);
+      reinterpret_cast<u32x4*>(dst)[lane] = reinterpret_cast<const u32x4*>(r)[lane];
+    }
   }
 }
 
@@ -150,7 +188,7 @@ hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
                                   uint8_t* cache, int64_t num_slots, const PageAddr& pa,
                                   bool f16_input, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const dim3 grid((uint32_t)((num_tokens + 3) / 4));
+  const dim3 grid((uint32_t)((num_tokens + 4 * kTokW - 1) / (4 * kTokW)));
   if (pa.record_bytes == Fmt432::kBytes) {
     if (f16_input) return hipErrorInvalidValue;    // rejected by the caller already
     hipLaunchKernelGGL((quantize_append_kernel<false, Fmt432>), grid, dim3(256), 0, stream,
