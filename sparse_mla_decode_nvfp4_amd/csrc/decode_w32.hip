@@ -39,6 +39,8 @@
 // XCD when the row count allows (the row's records stay in that XCD's L2).
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "kv_source.h"
 #include "launch.h"
@@ -809,12 +811,19 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
 template <bool kDual, class F, int kPairs>
 static hipError_t launch_w32_kernel(const DecodeArgs& a, int grid, hipStream_t stream) {
   constexpr size_t lds = LdsW32<kPairs>::kBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic-LDS limit is raised once per device (setting it again, as two
+  // threads may, is harmless)
+  constexpr int kDevices = 64;
+  static std::atomic<bool> attr_set[kDevices];
+  int dev = 0;
+  hipError_t ed = hipGetDevice(&dev);
+  if (ed != hipSuccess) return ed;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_w32_kernel<kDual, F, kPairs>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL((decode_w32_kernel<kDual, F, kPairs>), dim3(grid), dim3(128 * kPairs), lds, stream, a);
   return hipSuccess;
