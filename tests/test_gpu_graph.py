@@ -23,14 +23,16 @@ def records(n, rb, rep):
     return OC.quantize_records(f64(lat), f64(rope), rb)
 
 
-@pytest.mark.parametrize("h,splits,dual,rb", [
-    (16, 1, False, 352), (16, 3, False, 352), (32, 1, False, 352), (64, 4, False, 352),
-    (16, 2, True, 352), (64, 2, True, 352), (32, 3, False, 432), (16, 1, True, 432),
+@pytest.mark.parametrize("h,splits,dual,rb,b", [
+    (16, 1, False, 352, 3), (16, 3, False, 352, 3), (32, 1, False, 352, 3), (64, 4, False, 352, 3),
+    (16, 2, True, 352, 3), (64, 2, True, 352, 3), (32, 3, False, 432, 3), (16, 1, True, 432, 3),
+    # 1024 and 2048 workgroups: the 32-head kernel's two-pair shape
+    (64, 1, False, 352, 256), (64, 2, True, 352, 256),
 ])
-def test_captured_append_and_decode_replay_bit_exact(lib, h, splits, dual, rb):
-    note(f"graph h={h} splits={splits} dual={dual} record={rb}")
-    rng = np.random.default_rng(h * 7 + splits + rb)
-    b, s_q, k0, k1 = 3, 2, 300, 200
+def test_captured_append_and_decode_replay_bit_exact(lib, h, splits, dual, rb, b):
+    note(f"graph h={h} splits={splits} dual={dual} record={rb} batch={b}")
+    rng = np.random.default_rng(h * 7 + splits + rb + b)
+    s_q, k0, k1 = 2, 300, 200
     c0 = torch.from_numpy(records(1024, rb, 1).reshape(16, 64, rb)).to(DEV)
     c1 = torch.from_numpy(records(512, rb, 2).reshape(256, 2, rb)).to(DEV)
     q = torch.from_numpy(rng.standard_normal((b, s_q, h, 576)).astype(np.float32)).to(torch.bfloat16).to(DEV)
