@@ -300,6 +300,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
     a.indices1 = extra->indices;
   }
   a.rows = (int32_t)rows;
+  a.s_q = s_q;
   a.h_q = h_q;
   a.topk = topk;
   a.sink = attn_sink;

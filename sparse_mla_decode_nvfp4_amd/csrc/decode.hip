@@ -214,12 +214,21 @@ decode_tile16_kernel(DecodeArgs a) {
   // work unit (row, 16-head group, split).  Workgroups are dealt to the 8
   // XCDs round-robin by blockIdx; when the row count allows, every workgroup
   // of row r goes to XCD r % 8, so its head groups share the row's records
-  // and the combine kernel finds its partials in that XCD's L2.
+  // and the combine kernel finds its partials in that XCD's L2.  With several
+  // query rows per sequence (and at least 8 sequences) the rows of sequence
+  // q go to XCD q % 8 instead: they share their most recent tokens.
   const int hgroups = a.h_q >> 4;
   int split, hg, row;
   {
     const int x = blockIdx.x;
-    if ((a.rows & 7) == 0) {
+    if (a.s_q > 1 && a.rows % (8 * a.s_q) == 0) {
+      int y = x >> 3;
+      split = y % a.splits;
+      y /= a.splits;
+      hg = y % hgroups;
+      const int r = y / hgroups;            // this XCD's r-th row
+      row = ((r / a.s_q) * 8 + (x & 7)) * a.s_q + r % a.s_q;
+    } else if ((a.rows & 7) == 0) {
       int y = x >> 3;
       split = y % a.splits;
       y /= a.splits;

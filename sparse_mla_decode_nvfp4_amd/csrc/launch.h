@@ -36,6 +36,7 @@ struct DecodeArgs {
   const int32_t* indices1;  // [rows, topk - topk0]
   int32_t topk0;
   int32_t rows;             // batch * s_q
+  int32_t s_q;              // query rows per sequence (consecutive rows)
   int32_t h_q;
   int32_t topk;             // length of the joined list
   const float* sink;        // [h_q] or null

@@ -274,3 +274,13 @@ def test_many_workgroups_every_row(lib, b, h, topk, splits, p_inval):
     o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
     assert_decode_close(o, lse, o_ref, l_ref, f"many workgroups h={h} splits={splits}")
     assert bool((o[3].cpu() == 0).all()) and bool(torch.isneginf(lse[3]).all())
+
+
+@pytest.mark.parametrize("b,s_q,h,topk,splits", [(8, 2, 16, 100, 1), (16, 3, 48, 70, 2), (8, 4, 16, 33, 1)])
+def test_sequences_of_several_rows_every_row(lib, b, s_q, h, topk, splits):
+    # at least 8 sequences of several query rows: the 16-head kernel places
+    # workgroups by sequence
+    note(f"sequences b={b} s_q={s_q} h={h} topk={topk} splits={splits}")
+    recs, q, idx, sink, nb, bs = small_case(57 + s_q, b, s_q, h, topk)
+    o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
+    assert_decode_close(o, lse, o_ref, l_ref, f"sequences s_q={s_q}")
