@@ -203,6 +203,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2)
 decode_tile16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * kVChunk];
   __shared__ __attribute__((aligned(16))) uint16_t ptile[16][kPRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ptile_lo[16][kPRow];   // P - fp16(P)
   __shared__ float tmax[kWaves][16];
   __shared__ float lsum[kWaves][16];
 
@@ -458,20 +459,38 @@ decode_tile16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; r++) p[r] = fast_exp2(s[r] - m_safe);
     l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) = u32x2{pack_h16x2(p[0], p[1]), pack_h16x2(p[2], p[3])};
+    // P as fp16 hi + lo parts, so PV carries P to about 2^-22
+    const h16x2 h01 = __builtin_convertvector(f32x2{p[0], p[1]}, h16x2);
+    const h16x2 h23 = __builtin_convertvector(f32x2{p[2], p[3]}, h16x2);
+    const f32x2 f01 = __builtin_convertvector(h01, f32x2), f23 = __builtin_convertvector(h23, f32x2);
+    *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) =
+        u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+    *reinterpret_cast<u32x2*>(&ptile_lo[n][16 * wave + 4 * g]) =
+        u32x2{pack_h16x2(p[0] - f01.x, p[1] - f01.y), pack_h16x2(p[2] - f23.x, p[3] - f23.y)};
     lds_barrier();                        // P and V tiles complete
 
     // ---- O[:, 128w .. 128w+127] += P V over the tile's 64 tokens
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
       const h16x8 pa = *reinterpret_cast<const h16x8*>(&ptile[n][32 * ks + 8 * g]);
+      const h16x8 pl = *reinterpret_cast<const h16x8*>(&ptile_lo[n][32 * ks + 8 * g]);
+      // two blocks at a time: both lo products, then both hi products
 #pragma unroll
-      for (int nb = 0; nb < 8; nb++) {
-        lds_b* const rb = (lds_b*)(size_t)vr_base + 2 * nb * kVChunk + 32 * ks * 16;
-        const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)rb);
-        const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(rb + 4 * 16));
-        const h16x8 bv = __builtin_bit_cast(h16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, acc_o[nb], 0, 0, 0);
+      for (int nb = 0; nb < 8; nb += 2) {
+        h16x8 bv[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          lds_b* const rb = (lds_b*)(size_t)vr_base + 2 * (nb + u) * kVChunk + 32 * ks * 16;
+          const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)rb);
+          const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(rb + 4 * 16));
+          bv[u] = __builtin_bit_cast(h16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+          acc_o[nb + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv[u], acc_o[nb + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+          acc_o[nb + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[u], acc_o[nb + u], 0, 0, 0);
       }
     }
     ok_cur = rn.ok;

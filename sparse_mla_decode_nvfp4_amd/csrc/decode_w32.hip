@@ -235,7 +235,16 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   int row, hgrp, split;
   {
     const int x = blockIdx.x;
-    if ((a.rows & 7) == 0) {
+    if (a.s_q > 1 && a.rows % (8 * a.s_q) == 0) {
+      // several query rows per sequence: sequence q's rows go to XCD q % 8
+      // (they share their most recent tokens)
+      int y = x >> 3;
+      split = y % a.splits;
+      y /= a.splits;
+      hgrp = y % hgroups;
+      const int r = y / hgroups;
+      row = ((r / a.s_q) * 8 + (x & 7)) * a.s_q + r % a.s_q;
+    } else if ((a.rows & 7) == 0) {
       int y = x >> 3;
       split = y % a.splits;
       y /= a.splits;
@@ -550,7 +559,9 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
 #pragma unroll
         for (int r = 0; r < 16; r++) acc_o[nb][r] *= ar[r];
     }
-    uint32_t pd[2][2];
+    // P as fp16 hi + lo parts (the lo part holds P - hi exactly to fp16's
+    // precision), so PV carries P to about 2^-22 instead of 2^-11
+    uint32_t pd[2][2], pl[2][2];
 #pragma unroll
     for (int b = 0; b < 2; b++) {
       const float ms = (m_use[b] == -INFINITY) ? 0.f : m_use[b];
@@ -560,8 +571,13 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
         p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], qscale[b], -ms));
         l_part[b] += p[r];
       }
-      pd[b][0] = pack_f16p(p[0], p[1]);
-      pd[b][1] = pack_f16p(p[2], p[3]);
+#pragma unroll
+      for (int w = 0; w < 2; w++) {
+        const f16x2 hi = __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, f16x2);
+        const f32x2 hf = __builtin_convertvector(hi, f32x2);          // exact
+        pd[b][w] = __builtin_bit_cast(uint32_t, hi);
+        pl[b][w] = pack_f16p(p[2 * w] - hf.x, p[2 * w + 1] - hf.y);
+      }
     }
     // P into the 32x32 operand layout: lane 16G+n takes head 16(G&1)+n,
     // tokens 8(G>>1)+0..7; tokens +0..3 sit in row 2(G>>1), +4..7 in row
@@ -571,15 +587,29 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     const auto c0 = __builtin_amdgcn_permlane16_swap(pd[0][0], pd[1][0], false, false);
     const auto c1 = __builtin_amdgcn_permlane16_swap(pd[0][1], pd[1][1], false, false);
     const f16x8 pA = __builtin_bit_cast(f16x8, u32x4{c0[0], c1[0], c0[1], c1[1]});
+    const auto e0 = __builtin_amdgcn_permlane16_swap(pl[0][0], pl[1][0], false, false);
+    const auto e1 = __builtin_amdgcn_permlane16_swap(pl[0][1], pl[1][1], false, false);
+    const f16x8 pL = __builtin_bit_cast(f16x8, u32x4{e0[0], e1[0], e0[1], e1[1]});
     // ---- O += P V on this half's output dims
+    // two blocks at a time: both lo products, then both hi products, so
+    // the two products into one accumulator are not back to back
 #pragma unroll
-    for (int nb = 0; nb < 8; nb++) {
-      const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)((lds_u8*)(size_t)rb[0][nb & 3] + 256 * (nb >> 2)));
-      const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)((lds_u8*)(size_t)rb[1][nb & 3] + 256 * (nb >> 2)));
-      const f16x8 bv = __builtin_bit_cast(f16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc_o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pA, bv, acc_o[nb], 0, 0, 0);
+    for (int nb = 0; nb < 8; nb += 2) {
+      f16x8 bv[2];
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((lds_u8*)(size_t)rb[0][(nb + u) & 3] + 256 * ((nb + u) >> 2)));
+        const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((lds_u8*)(size_t)rb[1][(nb + u) & 3] + 256 * ((nb + u) >> 2)));
+        bv[u] = __builtin_bit_cast(f16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; u++)
+        acc_o[nb + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pL, bv[u], acc_o[nb + u], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 2; u++)
+        acc_o[nb + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pA, bv[u], acc_o[nb + u], 0, 0, 0);
     }
   };
 

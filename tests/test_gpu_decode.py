@@ -276,10 +276,14 @@ def test_many_workgroups_every_row(lib, b, h, topk, splits, p_inval):
     assert bool((o[3].cpu() == 0).all()) and bool(torch.isneginf(lse[3]).all())
 
 
-@pytest.mark.parametrize("b,s_q,h,topk,splits", [(8, 2, 16, 100, 1), (16, 3, 48, 70, 2), (8, 4, 16, 33, 1)])
+@pytest.mark.parametrize("b,s_q,h,topk,splits", [
+    (8, 2, 16, 100, 1), (16, 3, 48, 70, 2), (8, 4, 16, 33, 1),
+    (8, 2, 64, 100, 3), (8, 3, 32, 70, 1), (512, 2, 32, 40, 1),
+])
 def test_sequences_of_several_rows_every_row(lib, b, s_q, h, topk, splits):
-    # at least 8 sequences of several query rows: the 16-head kernel places
-    # workgroups by sequence
+    # at least 8 sequences of several query rows: both kernels place
+    # workgroups by sequence (the last case also takes the 32-head kernel's
+    # two-pair shape)
     note(f"sequences b={b} s_q={s_q} h={h} topk={topk} splits={splits}")
     recs, q, idx, sink, nb, bs = small_case(57 + s_q, b, s_q, h, topk)
     o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
