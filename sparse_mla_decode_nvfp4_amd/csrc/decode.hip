@@ -25,8 +25,8 @@
 //     folded into the softmax scale (exact for every bf16 element within 2^31
 //     of its head's largest);
 //   * S^T = K Q^T per wave; the per-head tile maximum is exchanged through
-//     LDS so every wave applies the same running max; P (fp16, relative
-//     error 2^-12) goes to a shared P tile;
+//     LDS so every wave applies the same running max; P goes to two shared
+//     tiles as fp16 hi + lo parts (PV runs on both, P carried to ~2^-22);
 //   * wave w accumulates O[16 heads, dv 128w .. 128w+127] over all 64 tokens
 //     of the tile (V read back with ds_read_b64_tr_b16), so the O accumulator
 //     is 32 registers per lane and two workgroups fit per CU;

@@ -28,9 +28,10 @@
 //   * Q is converted to fp16 once per workgroup with a per-head power-of-two
 //     scale folded into the softmax scale (exact for every bf16 element
 //     within 2^31 of its head's largest) and read from LDS as MFMA operands;
-//   * P is rounded to fp16 for the PV product (relative error 2^-12); the
-//     running max is raised lazily, only when a score exceeds it by more than
-//     2^15 (P stays in fp16 range and rescales of O are rare);
+//   * P enters the PV product as fp16 hi + lo parts (two MFMAs per block,
+//     P carried to about 2^-22); the running max is raised lazily, only when
+//     a score exceeds it by more than 2^15 (P stays in fp16 range and
+//     rescales of O are rare);
 //   * the pairs merge their states through LDS at the end (pairwise sums: two
 //     rounds for four pairs, one for two), and each wave writes its share of
 //     the output dims.
