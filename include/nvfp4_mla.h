@@ -223,6 +223,11 @@ size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
  * h_q must be a multiple of 16 (1..16 * 16), topk in [1, 65536].
  * The decode is one kernel launch, plus one combine launch when more than
  * one split runs.
+ * Accuracy: K and V are exact; Q is exact for every element within 2^31 of
+ * its head's largest magnitude; scores and sums are fp32; P enters PV as
+ * fp16 hi + lo parts (about 2^-22 relative); O is rounded once to bf16 (with
+ * splits, partial O is held in fp16 or fp32 first).  The results are the
+ * same bits on every run and in graph replays.
  */
 int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int64_t num_blocks, int32_t block_size,
