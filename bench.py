@@ -368,7 +368,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
-              "requested). See DESIGN.md for how the decode would shard.", file=sys.stderr)
+              "requested): the decode would shard by rows, by heads, or by context with the combine "
+              "export merging the slices.", file=sys.stderr)
         sys.exit(2)
     import torch
     dev = "cuda:0"
