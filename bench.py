@@ -367,7 +367,7 @@ def cpu_baseline(W, name, budget_s=12.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested): the decode would shard by rows, by heads, or by context with the combine "
               "export merging the slices.", file=sys.stderr)
         sys.exit(2)
