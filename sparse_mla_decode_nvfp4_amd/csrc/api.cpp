@@ -134,10 +134,11 @@ int check_decode_shape(int32_t batch, int32_t s_q, int32_t h_q, int32_t topk) {
 }
 
 // Deterministic split choice: enough splits to give every CU work, no more
-// than the top-k list can feed.  The 32-head-group kernel runs one four-wave
-// workgroup per (row, 32 heads, split), one per CU, each of its two token
-// streams with at least one 32-token chunk; the 16-head tile kernel runs one
-// workgroup per (row, 16 heads, split), two per CU, at least one 64-token
+// than the top-k list can feed.  The 32-head-group kernel runs one workgroup
+// per (row, 32 heads, split), aiming at one per CU; its wave pairs each take a
+// token stream of 16-token chunks (four pairs, or two pairs at two
+// workgroups per CU once the grid is that large).  The 16-head tile kernel runs
+// one workgroup per (row, 16 heads, split), two per CU, at least one 64-token
 // tile each.
 int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
   const bool w32 = nvfp4::decode_uses_w32(h_q);
@@ -240,7 +241,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
                        size_t workspace_bytes_in, int32_t num_splits, int32_t record_bytes,
                        void* stream) {
   if (extra && (topk0 < 0 || extra->topk < 0 || topk0 > 65536 || extra->topk > 65536))
-    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d and extra_topk = %d must be >= 0",
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d and extra_topk = %d must be in [0, 65536]",
                 topk0, extra ? extra->topk : 0);
   const int32_t topk = topk0 + (extra ? extra->topk : 0);
   int rc = check_decode_shape(batch, s_q, h_q, topk);
@@ -333,7 +334,8 @@ int dequantize_gather_impl(const char* fn, const uint8_t* kv_cache, int64_t num_
     if (!slots || !out_bf16)
       return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "slots and out must be non-NULL");
     if (!aligned(out_bf16, 16) || !aligned(slots, 4))
-      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "out must be 16-byte aligned and slots 4-byte aligned");
     if (n > (int64_t)0x7FFFFFFF * 4)
       return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "n too large");
   }

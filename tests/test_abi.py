@@ -151,8 +151,9 @@ def dual(**kw):
 
 
 @pytest.mark.parametrize("kw, needle", [
-    (dict(topk=-1), ">= 0"),
-    (dict(xtopk=-5), ">= 0"),
+    (dict(topk=-1), "[0, 65536]"),
+    (dict(xtopk=-5), "[0, 65536]"),
+    (dict(xtopk=70000), "[0, 65536]"),
     (dict(topk=0, xtopk=0), "topk"),
     (dict(topk=60000, xtopk=6000), "topk"),
     (dict(xcache=NULL), "extra cache: kv_cache is NULL"),
@@ -187,6 +188,9 @@ def test_combine_and_gather_reject_bad_arguments():
     assert lib.nvfp4_mla_dequantize_gather(P16, 4, 64, 64 * 352, NULL, 3, P16, NULL) == m.ERR_INVALID_ARGUMENT
     assert lib.nvfp4_mla_dequantize_gather(P16, 4, 64, 64 * 352, P16, 3,
                                            ctypes.c_void_p(0x100008), NULL) == m.ERR_INVALID_ARGUMENT
+    assert lib.nvfp4_mla_dequantize_gather(P16, 4, 64, 64 * 352, ctypes.c_void_p(0x100002), 3,
+                                           P16, NULL) == m.ERR_INVALID_ARGUMENT
+    assert "slots 4-byte aligned" in m.last_error()
     out = ctypes.c_int32(0)
     assert lib.nvfp4_mla_sparse_decode_plan(1, 1, 12, 64, ctypes.byref(out)) == m.ERR_INVALID_ARGUMENT
     assert lib.nvfp4_mla_sparse_decode_plan(1, 1, 16, 64, None) == m.ERR_INVALID_ARGUMENT
