@@ -122,6 +122,36 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _same_device(device, **tensors):
+    """Raises unless every given tensor (None skipped) is on `device`: the
+    library receives raw pointers and cannot tell host from device memory."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}; expected {device}")
+
+
+def _outputs(out, lse, shape, device):
+    """Caller-supplied or new O (bf16 [*shape, 512]) and LSE (float32 shape)."""
+    if out is None:
+        out = torch.empty((*shape, V_DIM), dtype=torch.bfloat16, device=device)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (*shape, V_DIM)
+          or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous bf16 {[*shape, V_DIM]} tensor")
+    if lse is None:
+        lse = torch.empty(shape, dtype=torch.float32, device=device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 {list(shape)} tensor")
+    return out, lse
+
+
+def _workspace_bytes(workspace):
+    if workspace is None:
+        return 0
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.numel() * workspace.element_size()
+
+
 def _cache_geometry(kv_cache):
     """(num_blocks, block_size, block_stride_bytes) of a [blocks, block_size,
     R] uint8 cache tensor, R = 352 or 432 (pages may be padded: stride(0) >=
@@ -163,6 +193,9 @@ def quantize_append(latent, rope, slot_mapping, kv_cache):
         raise ValueError("slot_mapping must be int64 [N] matching latent/rope rows")
     if latent.stride(-1) != 1 or rope.stride(-1) != 1 or not slot_mapping.is_contiguous():
         raise ValueError("inner dimensions must be contiguous")
+    if latent.dim() != 2 or rope.dim() != 2 or latent.shape[1] < NOPE_DIM or rope.shape[1] < ROPE_DIM:
+        raise ValueError("latent must be [N, >=512] and rope [N, >=64]")
+    _same_device(kv_cache.device, latent=latent, rope=rope, slot_mapping=slot_mapping)
     nb, bs, stride = _cache_geometry(kv_cache)
     if _ds(kv_cache):
         if latent.dtype != torch.bfloat16:
@@ -184,6 +217,9 @@ def dequantize_gather(kv_cache, slots, out=None):
     n = slots.numel()
     if out is None:
         out = torch.empty((n, QK_DIM), dtype=torch.bfloat16, device=kv_cache.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (n, QK_DIM) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 [{n}, {QK_DIM}] tensor")
+    _same_device(kv_cache.device, slots=slots, out=out)
     nb, bs, stride = _cache_geometry(kv_cache)
     fn = "nvfp4_mla_dequantize_gather" + _ds(kv_cache)
     code = getattr(lib(), fn)(_ptr(kv_cache), nb, bs, stride, _ptr(slots), n,
@@ -222,21 +258,20 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
     topk = indices.shape[2]
     if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
         raise ValueError("sink must be float32 [H]")
+    out, lse = _outputs(out, lse, (b, s, h), q.device)
+    _same_device(q.device, kv_cache=kv_cache, indices=indices, sink=sink, workspace=workspace,
+                 out=out, lse=lse)
     if num_splits == 0:
         num_splits = plan(b, s, h, topk)
     need = workspace_size(b, s, h, topk, num_splits)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((b, s, h), dtype=torch.float32, device=q.device)
     nb, bs, stride = _cache_geometry(kv_cache)
     fn = "nvfp4_mla_sparse_decode" + _ds(kv_cache)
     code = getattr(lib(), fn)(
         _ptr(q), _ptr(kv_cache), nb, bs, stride, _ptr(indices), b, s, h, topk, _ptr(sink),
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-        workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
+        _workspace_bytes(workspace), num_splits, _stream(q.device))
     _check(fn, code)
     return out, lse
 
@@ -261,15 +296,14 @@ def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, soft
     topk1 = _index_list(extra_indices, b, s, "extra_indices")
     if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
         raise ValueError("sink must be float32 [H]")
+    out, lse = _outputs(out, lse, (b, s, h), q.device)
+    _same_device(q.device, kv_cache=kv_cache, indices=indices, extra_kv_cache=extra_kv_cache,
+                 extra_indices=extra_indices, sink=sink, workspace=workspace, out=out, lse=lse)
     if num_splits == 0:
         num_splits = plan(b, s, h, topk0 + topk1)
     need = workspace_size(b, s, h, topk0 + topk1, num_splits)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((b, s, h, V_DIM), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((b, s, h), dtype=torch.float32, device=q.device)
     nb0, bs0, st0 = _cache_geometry(kv_cache)
     nb1, bs1, st1 = _cache_geometry(extra_kv_cache)
     if kv_cache.shape[2] != extra_kv_cache.shape[2]:
@@ -279,7 +313,7 @@ def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, soft
         _ptr(q), _ptr(kv_cache), nb0, bs0, st0, _ptr(indices) if topk0 else None, topk0,
         _ptr(extra_kv_cache), nb1, bs1, st1, _ptr(extra_indices) if topk1 else None, topk1,
         b, s, h, _ptr(sink), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-        workspace.numel() if workspace is not None else 0, num_splits, _stream(q.device))
+        _workspace_bytes(workspace), num_splits, _stream(q.device))
     _check(fn, code)
     return out, lse
 
@@ -287,13 +321,17 @@ def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, soft
 def combine(o_partial, lse_partial, sink=None, out=None, lse=None):
     """LSE-weighted merge.  o_partial float32 [P, R, H, 512], lse_partial float32
     [P, R, H].  Returns (O bf16 [R, H, 512], LSE float32 [R, H])."""
+    if o_partial.dtype != torch.float32 or o_partial.dim() != 4 or o_partial.shape[-1] != V_DIM:
+        raise ValueError("o_partial must be float32 [P, R, H, 512]")
+    p, r, h, _ = o_partial.shape
+    if lse_partial.dtype != torch.float32 or tuple(lse_partial.shape) != (p, r, h):
+        raise ValueError("lse_partial must be float32 [P, R, H] matching o_partial")
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
+        raise ValueError("sink must be float32 [H]")
     o_partial = o_partial.contiguous()
     lse_partial = lse_partial.contiguous()
-    p, r, h, _ = o_partial.shape
-    if out is None:
-        out = torch.empty((r, h, V_DIM), dtype=torch.bfloat16, device=o_partial.device)
-    if lse is None:
-        lse = torch.empty((r, h), dtype=torch.float32, device=o_partial.device)
+    out, lse = _outputs(out, lse, (r, h), o_partial.device)
+    _same_device(o_partial.device, lse_partial=lse_partial, sink=sink, out=out, lse=lse)
     code = lib().nvfp4_mla_combine(_ptr(o_partial), _ptr(lse_partial),
                                    p, r, h, _ptr(sink), _ptr(out), _ptr(lse),
                                    _stream(o_partial.device))

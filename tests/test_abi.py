@@ -231,3 +231,61 @@ def test_workspace_too_small_is_its_own_error():
     # the device gate comes before the workspace check, so on a GPU-less host
     # this reports the gate; the dedicated code is exercised in the GPU tests
     assert dec(splits=4, ws=NULL, ws_bytes=0) == m.ERR_UNSUPPORTED_DEVICE
+
+
+def _decode_args():
+    q = torch.zeros((2, 1, 16, 576), dtype=torch.bfloat16)
+    cache = torch.zeros((4, 64, 352), dtype=torch.uint8)
+    idx = torch.zeros((2, 1, 8), dtype=torch.int32)
+    return q, cache, idx
+
+
+META = torch.device("meta")
+
+
+@pytest.mark.parametrize("change, needle", [
+    (dict(out=torch.zeros((2, 1, 16, 256), dtype=torch.bfloat16)), "out must be"),
+    (dict(out=torch.zeros((2, 1, 16, 512), dtype=torch.float32)), "out must be"),
+    (dict(lse=torch.zeros((2, 1, 16), dtype=torch.float16)), "lse must be"),
+    (dict(lse=torch.zeros((2, 16), dtype=torch.float32)), "lse must be"),
+    (dict(kv_cache=torch.zeros((4, 64, 352), dtype=torch.uint8, device=META)), "kv_cache is on meta"),
+    (dict(indices=torch.zeros((2, 1, 8), dtype=torch.int32, device=META)), "indices is on meta"),
+    (dict(sink=torch.zeros(16, dtype=torch.float32, device=META)), "sink is on meta"),
+    (dict(workspace=torch.zeros(1024, dtype=torch.uint8, device=META)), "workspace is on meta"),
+])
+def test_binding_checks_caller_tensors_before_any_library_call(change, needle):
+    """The library takes raw pointers, so a tensor of the wrong shape, dtype
+    or device would be read or written out of bounds; the binding refuses it
+    first (on a machine without a GPU too: no library call is reached)."""
+    q, cache, idx = _decode_args()
+    kw = dict(q=q, kv_cache=cache, indices=idx, softmax_scale=0.1)
+    kw.update(change)
+    with pytest.raises(ValueError, match=needle):
+        m.sparse_decode(**kw)
+
+
+def test_binding_checks_dual_combine_append_and_gather_tensors():
+    q, cache, idx = _decode_args()
+    with pytest.raises(ValueError, match="extra_indices is on meta"):
+        m.sparse_decode_dual(q, cache, idx, cache, idx.to(META), 0.1)
+    with pytest.raises(ValueError, match="extra_kv_cache is on meta"):
+        m.sparse_decode_dual(q, cache, idx, cache.to(META), idx, 0.1)
+    o = torch.zeros((2, 3, 16, 512), dtype=torch.float32)
+    with pytest.raises(ValueError, match="lse_partial"):
+        m.combine(o, torch.zeros((2, 3, 8), dtype=torch.float32))
+    with pytest.raises(ValueError, match="o_partial"):
+        m.combine(o.half(), torch.zeros((2, 3, 16), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out must be"):
+        m.combine(o, torch.zeros((2, 3, 16)), out=torch.zeros((3, 16, 512), dtype=torch.float32))
+    with pytest.raises(ValueError, match="sink"):
+        m.combine(o, torch.zeros((2, 3, 16)), sink=torch.zeros(8))
+    lat = torch.zeros((4, 512), dtype=torch.bfloat16)
+    rope = torch.zeros((4, 64), dtype=torch.bfloat16)
+    slots = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError, match=r"\[N, >=512\]"):
+        m.quantize_append(lat[:, :256], rope, slots, cache)
+    with pytest.raises(ValueError, match="slot_mapping is on meta"):
+        m.quantize_append(lat, rope, slots.to(META), cache)
+    with pytest.raises(ValueError, match="out must be"):
+        m.dequantize_gather(cache, torch.zeros(4, dtype=torch.int32),
+                            out=torch.zeros((4, 512), dtype=torch.bfloat16))
