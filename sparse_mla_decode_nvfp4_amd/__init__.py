@@ -130,6 +130,14 @@ def _same_device(device, **tensors):
             raise ValueError(f"{name} is on {t.device}; expected {device}")
 
 
+def _check_sink(sink, h):
+    """The sink is read as h_q consecutive floats: a strided view would hand
+    the kernels the wrong values."""
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h
+                             or not sink.is_contiguous()):
+        raise ValueError("sink must be a contiguous float32 [H] tensor")
+
+
 def _outputs(out, lse, shape, device):
     """Caller-supplied or new O (bf16 [*shape, 512]) and LSE (float32 shape)."""
     if out is None:
@@ -256,8 +264,7 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
             or not indices.is_contiguous()):
         raise ValueError("indices must be a contiguous int32 [B, S_q, topk] tensor")
     topk = indices.shape[2]
-    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
-        raise ValueError("sink must be float32 [H]")
+    _check_sink(sink, h)
     out, lse = _outputs(out, lse, (b, s, h), q.device)
     _same_device(q.device, kv_cache=kv_cache, indices=indices, sink=sink, workspace=workspace,
                  out=out, lse=lse)
@@ -294,8 +301,7 @@ def sparse_decode_dual(q, kv_cache, indices, extra_kv_cache, extra_indices, soft
     b, s, h, _ = q.shape
     topk0 = _index_list(indices, b, s, "indices")
     topk1 = _index_list(extra_indices, b, s, "extra_indices")
-    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
-        raise ValueError("sink must be float32 [H]")
+    _check_sink(sink, h)
     out, lse = _outputs(out, lse, (b, s, h), q.device)
     _same_device(q.device, kv_cache=kv_cache, indices=indices, extra_kv_cache=extra_kv_cache,
                  extra_indices=extra_indices, sink=sink, workspace=workspace, out=out, lse=lse)
@@ -326,8 +332,7 @@ def combine(o_partial, lse_partial, sink=None, out=None, lse=None):
     p, r, h, _ = o_partial.shape
     if lse_partial.dtype != torch.float32 or tuple(lse_partial.shape) != (p, r, h):
         raise ValueError("lse_partial must be float32 [P, R, H] matching o_partial")
-    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != h):
-        raise ValueError("sink must be float32 [H]")
+    _check_sink(sink, h)
     o_partial = o_partial.contiguous()
     lse_partial = lse_partial.contiguous()
     out, lse = _outputs(out, lse, (r, h), o_partial.device)

@@ -252,6 +252,8 @@ META = torch.device("meta")
     (dict(indices=torch.zeros((2, 1, 8), dtype=torch.int32, device=META)), "indices is on meta"),
     (dict(sink=torch.zeros(16, dtype=torch.float32, device=META)), "sink is on meta"),
     (dict(workspace=torch.zeros(1024, dtype=torch.uint8, device=META)), "workspace is on meta"),
+    # a strided view: the kernels read sink[h] as consecutive floats
+    (dict(sink=torch.zeros((16, 2), dtype=torch.float32)[:, 0]), "contiguous float32"),
 ])
 def test_binding_checks_caller_tensors_before_any_library_call(change, needle):
     """The library takes raw pointers, so a tensor of the wrong shape, dtype
@@ -279,6 +281,11 @@ def test_binding_checks_dual_combine_append_and_gather_tensors():
         m.combine(o, torch.zeros((2, 3, 16)), out=torch.zeros((3, 16, 512), dtype=torch.float32))
     with pytest.raises(ValueError, match="sink"):
         m.combine(o, torch.zeros((2, 3, 16)), sink=torch.zeros(8))
+    with pytest.raises(ValueError, match="contiguous float32"):
+        m.combine(o, torch.zeros((2, 3, 16)), sink=torch.zeros((16, 2))[:, 1])
+    with pytest.raises(ValueError, match="contiguous float32"):
+        m.sparse_decode_dual(q, cache, idx, cache, idx, 0.1,
+                             sink=torch.zeros((16, 3), dtype=torch.float32)[:, 2])
     lat = torch.zeros((4, 512), dtype=torch.bfloat16)
     rope = torch.zeros((4, 64), dtype=torch.bfloat16)
     slots = torch.zeros(4, dtype=torch.int64)
