@@ -239,6 +239,31 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int32_t num_splits, void* stream);
 
 /*
+ * Allocation-free sparse decode, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): nvfp4_mla_sparse_decode without the workspace
+ * arguments.  Split partials go to a static device array of
+ * NVFP4_MLA_NOALLOC_SCRATCH_BYTES held by the library, one per GPU, looked
+ * up on the first call on each device and kept until the process ends; the
+ * call allocates and frees nothing.  Arguments, results and errors are those
+ * of nvfp4_mla_sparse_decode; a decode whose split partials
+ * (nvfp4_mla_sparse_decode_workspace_size for the chosen split count) exceed
+ * the array returns NVFP4_MLA_ERR_WORKSPACE_TOO_SMALL before any launch.
+ * Every call on one GPU shares that GPU's array (it needs no clearing: each
+ * call writes the partials it reads), so calls that may overlap on one GPU,
+ * on different streams or threads, race and must be serialised by the
+ * caller.
+ */
+#define NVFP4_MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int nvfp4_mla_sparse_decode_noalloc(const void* q_bf16, const uint8_t* kv_cache,
+                                    int64_t num_blocks, int32_t block_size,
+                                    int64_t block_stride_bytes, const int32_t* indices,
+                                    int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
+                                    const float* attn_sink, float softmax_scale,
+                                    void* out_bf16, float* lse, int32_t num_splits,
+                                    void* stream);
+
+/*
  * Sparse decode over a cache of 432-byte records: the attention of
  * nvfp4_mla_sparse_decode, with K the record's dequantized NoPE followed by
  * its bf16 RoPE.  Arguments, workspace (nvfp4_mla_sparse_decode_plan and

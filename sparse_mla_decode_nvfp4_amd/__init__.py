@@ -53,6 +53,8 @@ SIGNATURES = {
                                                     _P, _I64, _I32, _I64, _P, _I32,
                                                     _I32, _I32, _I32, _P, _F32, _P, _P, _P, _SZ,
                                                     _I32, _P]),
+    "nvfp4_mla_sparse_decode_noalloc": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32, _I32,
+                                                       _I32, _I32, _P, _F32, _P, _P, _I32, _P]),
     "nvfp4_mla_quantize_append_ds_mla": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P,
                                                         _I64, _I32, _I64, _P]),
     "nvfp4_mla_dequantize_gather_ds_mla": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _I64, _P,
@@ -280,6 +282,30 @@ def sparse_decode(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
         _workspace_bytes(workspace), num_splits, _stream(q.device))
     _check(fn, code)
+    return out, lse
+
+
+def sparse_decode_noalloc(q, kv_cache, indices, softmax_scale, sink=None, num_splits=0,
+                          out=None, lse=None):
+    """The decode of sparse_decode through the allocation-free entry point:
+    split partials live in the library's static per-GPU scratch array, so no
+    workspace is passed (or allocated here when out and lse are given).
+    352-byte records only.  Calls that may overlap on one GPU race on that
+    array.  Returns (O, LSE) as sparse_decode does."""
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[-1] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [B, S_q, H, 576] tensor")
+    b, s, h, _ = q.shape
+    topk = _index_list(indices, b, s, "indices")
+    _check_sink(sink, h)
+    out, lse = _outputs(out, lse, (b, s, h), q.device)
+    _same_device(q.device, kv_cache=kv_cache, indices=indices, sink=sink, out=out, lse=lse)
+    nb, bs, stride = _cache_geometry(kv_cache)
+    if _ds(kv_cache):
+        raise ValueError("the allocation-free entry point reads 352-byte records")
+    code = lib().nvfp4_mla_sparse_decode_noalloc(
+        _ptr(q), _ptr(kv_cache), nb, bs, stride, _ptr(indices), b, s, h, topk, _ptr(sink),
+        float(softmax_scale), _ptr(out), _ptr(lse), num_splits, _stream(q.device))
+    _check("nvfp4_mla_sparse_decode_noalloc", code)
     return out, lse
 
 

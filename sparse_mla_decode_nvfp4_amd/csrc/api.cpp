@@ -12,6 +12,7 @@
 
 #include <atomic>
 #include <algorithm>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -181,6 +182,42 @@ size_t workspace_bytes(int64_t rows, int32_t h_q, int32_t splits) {
 
 }  // namespace
 
+// Split-partial scratch of nvfp4_mla_sparse_decode_noalloc: one array per GPU
+// the library runs on, held until the process ends.  Its name is a host-side
+// stand-in in host code; only the address hipGetSymbolAddress returns for the
+// current device is ever passed to a kernel.
+namespace {
+constexpr size_t kScratchBytes = NVFP4_MLA_NOALLOC_SCRATCH_BYTES;
+}
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];     // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) on its first use.
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_MLA_ERR_UNSUPPORTED_DEVICE, "no usable HIP device (%s)", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(NVFP4_MLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_MLA_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // Shared by the bf16 and fp16 exports: the same checks, one kernel template.
@@ -239,7 +276,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
                        int32_t batch, int32_t s_q, int32_t h_q, const float* attn_sink,
                        float softmax_scale, void* out_bf16, float* lse, void* workspace,
                        size_t workspace_bytes_in, int32_t num_splits, int32_t record_bytes,
-                       void* stream) {
+                       void* stream, bool static_scratch = false) {
   if (extra && (topk0 < 0 || extra->topk < 0 || topk0 > 65536 || extra->topk > 65536))
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d and extra_topk = %d must be in [0, 65536]",
                 topk0, extra ? extra->topk : 0);
@@ -278,6 +315,17 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   if (rc) return rc;
   int splits = num_splits == 0 ? plan_splits((int32_t)rows, h_q, topk, cus) : num_splits;
   const size_t need = workspace_bytes(rows, h_q, splits);
+  if (static_scratch && need > 0) {
+    if (need > kScratchBytes)
+      return fail(NVFP4_MLA_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: a decode of %lld rows x %d heads with %d splits needs %zu bytes of split "
+                  "partials; the allocation-free entry point holds at most %zu (use fewer splits "
+                  "or nvfp4_mla_sparse_decode with a workspace)",
+                  fn, (long long)rows, h_q, splits, need, kScratchBytes);
+    rc = device_scratch(&workspace);
+    if (rc) return rc;
+    workspace_bytes_in = kScratchBytes;
+  }
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes_in < need)
       return fail(NVFP4_MLA_ERR_WORKSPACE_TOO_SMALL,
@@ -461,6 +509,18 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache, int64_t
                             block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
                             attn_sink, softmax_scale, out_bf16, lse, workspace,
                             workspace_bytes_in, num_splits, NVFP4_MLA_RECORD_BYTES, stream);
+}
+
+int nvfp4_mla_sparse_decode_noalloc(const void* q_bf16, const uint8_t* kv_cache,
+                                    int64_t num_blocks, int32_t block_size,
+                                    int64_t block_stride_bytes, const int32_t* indices,
+                                    int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
+                                    const float* attn_sink, float softmax_scale, void* out_bf16,
+                                    float* lse, int32_t num_splits, void* stream) {
+  return sparse_decode_impl("sparse_decode_noalloc", q_bf16, kv_cache, num_blocks, block_size,
+                            block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
+                            attn_sink, softmax_scale, out_bf16, lse, nullptr, 0, num_splits,
+                            NVFP4_MLA_RECORD_BYTES, stream, /*static_scratch=*/true);
 }
 
 int nvfp4_mla_sparse_decode_ds_mla(const void* q_bf16, const uint8_t* kv_cache,

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = m.lib()
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
         assert name in m.SIGNATURES, name
@@ -135,6 +135,36 @@ def dec(**kw):
 def test_sparse_decode_rejects_bad_arguments(kw, needle):
     assert dec(**kw) == m.ERR_INVALID_ARGUMENT
     assert needle in m.last_error()
+
+
+def dec_noalloc(**kw):
+    a = dict(q=P16, cache=P16, nblocks=4, bs=64, stride=64 * 352, idx=P16, batch=2, s_q=1,
+             h_q=16, topk=64, sink=NULL, scale=0.04, out=P16, lse=P16, splits=1, stream=NULL)
+    a.update(kw)
+    return m.lib().nvfp4_mla_sparse_decode_noalloc(
+        a["q"], a["cache"], a["nblocks"], a["bs"], a["stride"], a["idx"], a["batch"], a["s_q"],
+        a["h_q"], a["topk"], a["sink"], a["scale"], a["out"], a["lse"], a["splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw, needle", [
+    (dict(h_q=24), "multiple of 16"),
+    (dict(topk=0), "topk"),
+    (dict(cache=NULL), "kv_cache"),
+    (dict(stride=64 * 352 - 16), "block_size * 352"),
+    (dict(splits=65), "num_splits"),
+    (dict(q=NULL), "non-NULL"),
+    (dict(lse=ctypes.c_void_p(0x100002)), "aligned"),
+])
+def test_sparse_decode_noalloc_rejects_bad_arguments(kw, needle):
+    assert dec_noalloc(**kw) == m.ERR_INVALID_ARGUMENT
+    assert needle in m.last_error()
+
+
+def test_sparse_decode_noalloc_without_a_gpu_reports_the_device_gate():
+    if torch.cuda.device_count() > 0:
+        pytest.skip("device-gate check is for GPU-less hosts")
+    assert dec_noalloc() == m.ERR_UNSUPPORTED_DEVICE
+    assert dec_noalloc(splits=4) == m.ERR_UNSUPPORTED_DEVICE
 
 
 def dual(**kw):
