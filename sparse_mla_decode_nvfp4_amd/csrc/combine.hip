@@ -3,7 +3,8 @@
 // end.  For partial results (O_i, LSE_i) (O_i sink-free and normalised within
 // its subset, LSE_i = ln of its softmax denominator):
 //   LSE = ln sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) O_i / (1 + exp(sink - LSE)).
-// An all-empty row (every LSE_i = -inf) gives O = 0, LSE = -inf.
+// An all-empty row (every LSE_i = -inf) gives O = 0, LSE = -inf; a NaN LSE_i
+// gives a NaN row.
 #include <math.h>
 
 #include "device_common.h"
@@ -66,6 +67,9 @@ combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
   // partial loads are issued together
   float m = -INFINITY, tot = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // a NaN partial LSE (a decode workgroup that marked its result as failed)
+  // makes the merged row NaN rather than being skipped by the maxima
+  bool nan_seen = false;
   for (int s0 = 0; s0 < splits; s0 += 4) {
     float ls[4];
     float v[4][8];
@@ -81,6 +85,7 @@ combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
         for (int i = 0; i < 8; i++) v[u][i] = 0.f;
       }
     }
+    nan_seen |= (ls[0] != ls[0]) | (ls[1] != ls[1]) | (ls[2] != ls[2]) | (ls[3] != ls[3]);
     const float mn = fmaxf(m, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
     if (mn == -INFINITY) continue;
     if (mn != m) {
@@ -97,6 +102,14 @@ combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
 #pragma unroll
       for (int i = 0; i < 8; i++) acc[i] = __builtin_fmaf(w, v[u][i], acc[i]);
     }
+  }
+  if (nan_seen) {
+    const float qnan = __builtin_nanf("");
+    const uint32_t nb = 0x7FC07FC0u;               // two bf16 quiet NaNs
+    reinterpret_cast<u32x2*>(orow)[0] = u32x2{nb, nb};
+    reinterpret_cast<u32x2*>(orow)[1] = u32x2{nb, nb};
+    if (lane == 0) lse[rh] = qnan;
+    return;
   }
   if (m == -INFINITY) {
     reinterpret_cast<u32x2*>(orow)[0] = u32x2{0u, 0u};

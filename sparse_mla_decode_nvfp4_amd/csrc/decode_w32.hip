@@ -66,6 +66,7 @@ constexpr int kVTileP = kChunkP * kVRowP;          // 8 KB per wave
 constexpr int kXsBytes = 2 * 64 * 16;              // partial S^T of one wave: 2 KB
 constexpr int kQBytes = 2 * 2 * 9 * 64 * 16;       // Q operands: [half][block][k-step][lane]
 constexpr float kLazyP = 15.0f;                    // P = 2^(s - m_run) <= 2^15
+constexpr int kSpinLimit = 1 << 22;                // polls of a partner wait (~0.1 s)
 constexpr float kLn2P = 0.6931471805599453f;
 constexpr float kLog2eP = 1.4426950408889634f;
 
@@ -82,7 +83,9 @@ struct LdsW32 {
   static constexpr int kOffQ = kOffXs + kXsBufs * kWaves * kXsBytes;
   static constexpr int kOffStat = kOffQ + kQBytes;
   static constexpr int kOffFlag = kOffStat + kWaves * 2 * 32 * 4 + 2 * 32 * 4;
-  static constexpr int kBytes = kOffFlag + 2 * kWaves * 4;     // published, consumed
+  // published and consumed counters per wave, then the lost-wait flag
+  static constexpr int kOffFail = kOffFlag + 2 * kWaves * 4;
+  static constexpr int kBytes = kOffFail + 16;
   // merge: 4 slots of 4 KB per wave in round one, then an 8 KB output
   // stage per wave (past the round-two slots for four pairs, from 0 for two)
   static constexpr int kOffStage = kPairs == 4 ? 16 * 4096 : 0;
@@ -217,6 +220,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   lds_u32* const qmax = (lds_u32*)(lds + L::kOffStat + kWavesP * 2 * 32 * 4); // [half][32]
   lds_u32* const flag = (lds_u32*)(lds + L::kOffFlag);   // [wave]: chunks whose partial S is published
   lds_u32* const consumed = flag + kWavesP;              // [wave]: partner chunks read (one buffer)
+  lds_u32* const failed = (lds_u32*)(lds + L::kOffFail); // a wave gave up waiting for its partner
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -332,6 +336,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     if (lane == 0) {
       flag[wave] = 0;
       consumed[wave] = 0;
+      if (wave == 0) *failed = 0;
     }
     lds_sync_p();
     int pq[2];
@@ -412,6 +417,10 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   // bytes (raw index nxt_raw, loaded a chunk earlier) right after its use.
   f32x4 sacc[2];
   uint32_t okbits = 0;   // bit r: token 4g+r of the current chunk takes part
+  // A partner wait that runs out of polls (correct execution never gets
+  // near the limit) sets `lost`; the workgroup then writes NaN O and LSE
+  // instead of results built from a partial S that may be stale.
+  bool lost = false;
   auto pre = [&](RawP<F>& cur, bool& cur_ok, int32_t& nxt_raw, int pos) {
     const int32_t nxt2_raw = load_idx(cid2);
     const bool v = cur_ok;
@@ -478,10 +487,15 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     if constexpr (L::kXsBufs == 1) {
       // one buffer: the partner must have read this wave's previous chunk
       // (bounded: it reads it right after its own exchange write)
-      for (int it = 0; it < (1 << 22); it++) {
-        if ((int)__hip_atomic_load(consumed + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= pos) break;
+      bool seen = false;
+      for (int it = 0; it < kSpinLimit; it++) {
+        if ((int)__hip_atomic_load(consumed + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= pos) {
+          seen = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
+      lost |= !seen;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     }
 #pragma unroll
@@ -498,10 +512,15 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   // wait until the partner has published chunk pos (bounded: the partner
   // runs the same number of chunks in the same workgroup)
   auto pair_wait = [&](int pos) {
-    for (int it = 0; it < (1 << 22); it++) {
-      if ((int)__hip_atomic_load(flag + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > pos) break;
+    bool seen = false;
+    for (int it = 0; it < kSpinLimit; it++) {
+      if ((int)__hip_atomic_load(flag + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > pos) {
+        seen = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
+    lost |= !seen;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
@@ -641,6 +660,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   }
 
   // ---- merge the four pairs (same heads and output dims, disjoint tokens)
+  if (lost && lane == 0) __hip_atomic_store(failed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   sum_blocks(l_part[0], l_part[1]);
   if (g == 0) {
 #pragma unroll
@@ -650,6 +670,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     }
   }
   lds_sync_p();
+  const bool wg_failed = *failed != 0u;
   float Mh[2], Lh[2], fown[2];
 #pragma unroll
   for (int b = 0; b < 2; b++) {
@@ -757,6 +778,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
       if (single && a.sink != nullptr && Lh[b] > 0.f)
         denom += __builtin_amdgcn_exp2f(a.sink[h0 + 16 * b + n] * kLog2eP - Mh[b]);
       invh[b] = Lh[b] > 0.f ? 1.0f / denom : 0.f;
+      if (wg_failed) invh[b] = __builtin_nanf("");
     }
 #pragma unroll
     for (int r = 0; r < 16; r++) {
@@ -832,7 +854,8 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   if (wave == 0 && g == 0) {
 #pragma unroll
     for (int b = 0; b < 2; b++) {
-      const float lse = Lh[b] > 0.f ? (Mh[b] + __log2f(Lh[b])) * kLn2P : -INFINITY;
+      float lse = Lh[b] > 0.f ? (Mh[b] + __log2f(Lh[b])) * kLn2P : -INFINITY;
+      if (wg_failed) lse = __builtin_nanf("");
       if (single) a.lse[orow + 16 * b + n] = lse;
       else a.lse_part[prow + 16 * b + n] = lse;
     }
