@@ -41,6 +41,8 @@ FLOP_PER_TOKEN_HEAD = 2 * (576 + 512)
 HEADLINE = "decode_h64"
 METRIC = "sparse decode TFLOP/s + KV GB/s, h_q 16/64/128, topk 2048; % of roofline"
 DECODE_SRC = os.path.join(ROOT, "sparse_mla_decode_nvfp4_amd", "csrc", "decode.hip")
+FLUSH_BYTES = 1 << 30          # scratch written before each cold-timed decode
+COLD_LAUNCHES = 50
 
 
 def parse():
@@ -254,6 +256,31 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         ev[k][1].record()
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    # cold: before each decode a 1 GiB scratch write evicts the 256 MB MALL
+    # and the L2s, so the decode's records come from HBM (median of the
+    # event-timed decodes).  The write leaves dirty lines that are written
+    # back while the decode runs; a second pass evicts with a 1 GiB read
+    # (clean lines) instead.
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    n_cold = min(steps, COLD_LAUNCHES)
+
+    def timed_after(evict):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_cold)]
+        sink_acc = torch.zeros((), dtype=torch.int64, device=dev)
+        for k in range(n_cold):
+            r = k % nsets
+            run_app(r)
+            evict(k, sink_acc)
+            evs[k][0].record()
+            run_dec(r)
+            evs[k][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    cold_ms = timed_after(lambda k, acc: flush.fill_(k + 1))
+    cold_read_ms = timed_after(lambda k, acc: acc.add_(flush.sum()))
+    del flush
     acc = decode_accounting(sets, wl)
     dec_avg = float(dec_ms.mean())
     res = dict(
@@ -262,6 +289,8 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         splits=splits, sets=nsets, ms_per_step=step_ms,
         decode_ms_mean=dec_avg, decode_ms_median=float(np.median(dec_ms)),
         decode_ms_min=float(dec_ms.min()),
+        cold_decode_ms_median=float(np.median(cold_ms)), cold_launches=n_cold,
+        cold_read_decode_ms_median=float(np.median(cold_read_ms)),
         flops_per_step=acc["flops"], kv_bytes_per_step=acc["kv_bytes"],
         compulsory_bytes_per_step=acc["unique_bytes"],
         step_tflops=acc["flops"] / (step_ms * 1e-3) / 1e12,
@@ -271,13 +300,24 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     )
     res["mfma_frac"] = res["decode_tflops"] / PEAK_BF16_TFLOPS
     res["hbm_frac"] = res["decode_hbm_gbps"] / PEAK_HBM_GBS
+    res["cold_decode_tflops"] = acc["flops"] / (res["cold_decode_ms_median"] * 1e-3) / 1e12
+    res["cold_decode_hbm_gbps"] = acc["unique_bytes"] / (res["cold_decode_ms_median"] * 1e-3) / 1e9
+    res["cold_mfma_frac"] = res["cold_decode_tflops"] / PEAK_BF16_TFLOPS
+    res["cold_hbm_frac"] = res["cold_decode_hbm_gbps"] / PEAK_HBM_GBS
+    res["invalid_frac"] = float(np.mean([np.mean(idx < 0) for s in sets
+                                         for idx, _ in index_lists(s)]))
+    res["block_size"] = ([p.block_size for p in pools] if dual else wl.block_size)
+    res["record_bytes"] = getattr(wl, "record_bytes", 352)
+    res["batch"], res["s_q"] = wl.batch, wl.s_q
+    res["sink"] = wl.sink is not None
     intensity = acc["flops"] / acc["unique_bytes"]
     res["bound"] = "mfma" if intensity > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
     log(f"{name}: step {step_ms * 1e3:.1f} us, decode {dec_avg * 1e3:.1f} us (median "
         f"{res['decode_ms_median'] * 1e3:.1f}), {res['decode_tflops']:.0f} TFLOP/s "
         f"({100 * res['mfma_frac']:.1f}% MFMA), KV {res['decode_kv_gbps']:.0f} GB/s, "
         f"compulsory {res['decode_hbm_gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
-        f"splits {splits}")
+        f"splits {splits}; cold median {res['cold_decode_ms_median'] * 1e3:.1f} us after a "
+        f"1 GiB write, {res['cold_read_decode_ms_median'] * 1e3:.1f} us after a 1 GiB read")
     del cache, caches, ws, inp, g_app, g_dec
     torch.cuda.empty_cache()
     return res
@@ -318,6 +358,27 @@ def bench_append(lib, W, steps, warmup, dev, fp16=False):
 
 
 # --------------------------------------------------------------------------- cpu
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it, from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def numpy_blas():
+    """The BLAS numpy was built against (name and version)."""
+    try:
+        cfg = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        return f"{cfg.get('name')} {cfg.get('version')}"
+    except (AttributeError, KeyError, TypeError):
+        return None
+
+
 def cpu_baseline(W, name, budget_s=12.0):
     """The oracle (numpy fp64) timed on this host: the step's quantize-append
     of its new tokens plus the decode of a bounded sample of query rows."""
@@ -358,6 +419,7 @@ def cpu_baseline(W, name, budget_s=12.0):
         done += 1
     cores = len(os.sched_getaffinity(0))
     return dict(value=flops / (t_app + t_dec) / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                cpu_model=cpu_model(), blas=numpy_blas(),
                 sample=f"{done} query-row decodes of {name} (its {rows} rows cycled; float64 numpy) "
                        f"plus the step's {rows}-token quantize-append; {t_app + t_dec:.1f} s",
                 seconds=t_app + t_dec)
@@ -448,16 +510,22 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": 32, "s_q": 1, "h_q": 64, "topk": 2048,
-                   "d_qk": 576, "d_v": 512, "record_bytes": 352, "block_size": 64,
-                   "invalid_frac": 0.05, "sink": True, "splits": head["splits"],
-                   "index_sets": args.sets, "timed_launches": "graph" if use_graph else "eager"},
+        "config": {"workload": args.workload, "batch": head["batch"], "s_q": head["s_q"],
+                   "h_q": head["h_q"], "topk": head["topk"], "d_qk": 576, "d_v": 512,
+                   "record_bytes": head["record_bytes"], "block_size": head["block_size"],
+                   "invalid_frac": round(head["invalid_frac"], 4), "sink": head["sink"],
+                   "splits": head["splits"], "index_sets": args.sets,
+                   "timed_launches": "graph" if use_graph else "eager"},
         "kv_gbps": head["kv_bytes_per_step"] / (head["ms_per_step"] * 1e-3) / 1e9,
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "kernel": head["kernel"] + ("+combine_kernel" if head["splits"] > 1 and
                                                  head["kernel"] != "decode_tile16_kernel" else ""),
                      "kernel_us_mean": head["decode_ms_mean"] * 1e3,
+                     "cold_kernel_us_median": head["cold_decode_ms_median"] * 1e3,
+                     "cold_read_kernel_us_median": head["cold_read_decode_ms_median"] * 1e3,
+                     "cold_frac": (head["cold_mfma_frac"] if bound == "mfma"
+                                   else head["cold_hbm_frac"]),
                      "other_resource_frac": head["hbm_frac"] if bound == "mfma" else head["mfma_frac"]},
         "cpu_baseline": cpu,
         "workloads": {args.workload: head, **extra},
