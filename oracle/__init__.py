@@ -16,12 +16,15 @@ Sources (cited by page title and section):
                  (scale = E4M3(group_amax/6), error bound, slot_mapping).
   [sglang-38646] "[SM120] Add opt-in NVFP4 sparse-MLA KV cache format for
                  DeepSeek-V4", Modifications (slot ids shared by writers and
-                 readers).
+                 readers) and Limitations (the fused norm + rope + quantize +
+                 store kernel).
 
 Modules:
   formats    -- element encodings: E2M1, E4M3 decode/encode, record layout.
   codec      -- quantize-append (write path) and record dequantization.
   attention  -- sparse MLA decode (O, LSE) and the split-KV combine.
+  norm_rope  -- the fused write path: RMSNorm + rotary embedding, rounded to
+                bf16, then the write rule.
 """
 
-from . import formats, codec, attention  # noqa: F401
+from . import formats, codec, attention, norm_rope  # noqa: F401
