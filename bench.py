@@ -323,30 +323,44 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     return res
 
 
-def bench_append(lib, W, steps, warmup, dev, fp16=False):
-    """The append_write workload through the bf16 export, or with the same
-    latents cast to fp16 through the fp16 export."""
+def bench_append(lib, W, steps, warmup, dev, fp16=False, fused=False):
+    """The append_write workload through the bf16 export, with the same
+    latents cast to fp16 through the fp16 export, or through the fused
+    norm + rotary + quantize export (un-normalised latents, a weight, a
+    rotary table and positions)."""
     import torch
     wl = W.append_write()
-    name = "append_write_fp16" if fp16 else "append_write"
+    name = "append_write_fp16" if fp16 else ("append_write_fused" if fused else "append_write")
     cache = torch.from_numpy(wl.sentinel.reshape(wl.num_blocks, wl.block_size, 352)).to(dev)
     lat, rope = wl.latent.to(dev), wl.rope.to(dev)
     if fp16:
         lat, rope = lat.to(torch.float16), rope.to(torch.float16)
     sm = torch.from_numpy(wl.slot_mapping).to(dev)
+    if fused:
+        nr = W.norm_rope_inputs(wl.num_tokens)
+        w, cs = nr.norm_weight.to(dev), nr.cos_sin.to(dev)
+        pos = torch.from_numpy(nr.positions).to(dev)
+
+        def run():
+            lib.norm_rope_quantize_append(lat, rope, w, nr.eps, cs, pos, sm, cache)
+    else:
+        def run():
+            lib.quantize_append(lat, rope, sm, cache)
     for _ in range(warmup):
-        lib.quantize_append(lat, rope, sm, cache)
+        run()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
     for k in range(steps):
         ev[k][0].record()
-        lib.quantize_append(lat, rope, sm, cache)
+        run()
         ev[k][1].record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     mapped = int((wl.slot_mapping >= 0).sum())
-    nbytes = mapped * (512 * 2 + 64 * 2 + 352) + wl.num_tokens * 8
+    # compulsory: each mapped token's inputs and record, every slot id (and,
+    # fused, its position; the weight and the table rows are cache-resident)
+    nbytes = mapped * (512 * 2 + 64 * 2 + 352) + wl.num_tokens * 8 * (2 if fused else 1)
     res = dict(workload=name, tokens=wl.num_tokens, mapped=mapped, ms=ms,
                bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9,
                tokens_per_s=mapped / (ms * 1e-3))
@@ -464,8 +478,9 @@ def main():
         return
 
     if args.only:
-        if args.only in ("append_write", "append_write_fp16"):
-            res = bench_append(lib, W, args.steps, args.warmup, dev, fp16=args.only.endswith("fp16"))
+        if args.only in ("append_write", "append_write_fp16", "append_write_fused"):
+            res = bench_append(lib, W, args.steps, args.warmup, dev, fp16=args.only.endswith("fp16"),
+                               fused=args.only.endswith("fused"))
         else:
             # a prefill's query rows already span its pool: one index set
             nsets = 1 if args.only.startswith("prefill") else args.sets
@@ -490,6 +505,8 @@ def main():
                                              max(5, args.warmup // 2), dev)
         extra["append_write_fp16"] = bench_append(lib, W, max(20, args.steps // 2),
                                                   max(5, args.warmup // 2), dev, fp16=True)
+        extra["append_write_fused"] = bench_append(lib, W, max(20, args.steps // 2),
+                                                   max(5, args.warmup // 2), dev, fused=True)
     cpu = None if args.no_cpu else cpu_baseline(W, args.workload)
 
     bound = head["bound"]

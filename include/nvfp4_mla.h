@@ -61,6 +61,10 @@
 extern "C" {
 #endif
 
+/* HIP's stream handle, declared as hip_runtime_api.h declares it (so either
+ * header may be included first); NULL is the null stream. */
+typedef struct ihipStream_t* hipStream_t;
+
 #define NVFP4_MLA_ABI_VERSION 1
 
 #define NVFP4_MLA_RECORD_BYTES 352
@@ -121,7 +125,7 @@ int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride
                               const int64_t* slot_mapping, int64_t num_tokens,
                               uint8_t* kv_cache, int64_t num_blocks,
                               int32_t block_size, int64_t block_stride_bytes,
-                              void* stream);
+                              hipStream_t stream);
 
 /*
  * Quantize-append from fp16 inputs: the same write rule and 352-byte record
@@ -137,7 +141,78 @@ int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_s
                                    const int64_t* slot_mapping, int64_t num_tokens,
                                    uint8_t* kv_cache, int64_t num_blocks,
                                    int32_t block_size, int64_t block_stride_bytes,
-                                   void* stream);
+                                   hipStream_t stream);
+
+/*
+ * Fused norm + rotary + quantize-append: one pass that normalises the latent,
+ * turns the RoPE part, rounds both to bf16 and writes the records by the rule
+ * of nvfp4_mla_quantize_append -- the store sglang PR #38646 "[SM120] opt-in
+ * NVFP4 sparse-MLA KV cache format for DeepSeek-V4" lists as missing under
+ * Limitations (without it the path pays a bf16 intermediate plus a separate
+ * quantize kernel).  Per token n with slot_mapping[n] >= 0 and
+ * 0 <= positions[n] < max_position:
+ *     y   = RMSNorm(latent[n]) = latent[n] * w / sqrt(mean(latent[n]^2) + eps)
+ *     k   = RoPE part turned by the angles of row positions[n] of cos_sin:
+ *           (a, b) -> (a cos_i - b sin_i, b cos_i + a sin_i) over the pairs
+ *           (2i, 2i+1) (rope_neox = 0, the DeepSeek layout) or (i, i+32)
+ *           (rope_neox = 1)
+ *     the 352-byte record of (bf16(y), bf16(k))
+ * The arithmetic is binary32, each step rounded to nearest even with no fused
+ * multiply-add, in a fixed order: squares; a sum of elements 8l..8l+7 in
+ * element order for l = 0..63; those 64 sums added pairwise, neighbours
+ * first; times 1/512; plus eps; sqrt; 1 / that; (x * r) * w; then products,
+ * then the difference or sum for the turn; bf16 = round to nearest even.
+ * The records are therefore exactly those nvfp4_mla_quantize_append writes
+ * from the bf16 intermediate an unfused norm and rotary step would store.
+ *
+ *   latent_bf16, rope_bf16  un-normalised latent [num_tokens, >= 512] and
+ *                    un-rotated RoPE [num_tokens, >= 64], bf16, with row
+ *                    strides in elements as for nvfp4_mla_quantize_append
+ *   norm_weight_bf16 [512] bf16 RMSNorm weight, 16-byte aligned
+ *   eps              finite, >= 0 (a zero latent row needs eps > 0)
+ *   cos_sin          [max_position, 64] float32 contiguous: cos of the 32
+ *                    frequencies, then their sin, per position
+ *   positions        [num_tokens] int64; a token whose position is outside
+ *                    [0, max_position) is not written, like slot -1
+ *   rope_neox        0 or 1 (pair layout above)
+ * slot_mapping, kv_cache and the page geometry are as for
+ * nvfp4_mla_quantize_append, whose skip rules and errors apply as well.
+ */
+int nvfp4_mla_norm_rope_quantize_append(const void* latent_bf16, int64_t latent_row_stride,
+                                        const void* rope_bf16, int64_t rope_row_stride,
+                                        const void* norm_weight_bf16, float eps,
+                                        const float* cos_sin, int64_t max_position,
+                                        const int64_t* positions, int32_t rope_neox,
+                                        const int64_t* slot_mapping, int64_t num_tokens,
+                                        uint8_t* kv_cache, int64_t num_blocks,
+                                        int32_t block_size, int64_t block_stride_bytes,
+                                        hipStream_t stream);
+
+/* The fused write path into 432-byte "nvfp4_ds_mla" records: the arguments
+ * and arithmetic of nvfp4_mla_norm_rope_quantize_append, the records those of
+ * nvfp4_mla_quantize_append_ds_mla (the turned RoPE stored as its bf16
+ * bits); block_stride_bytes >= block_size * 432. */
+int nvfp4_mla_norm_rope_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row_stride,
+                                               const void* rope_bf16, int64_t rope_row_stride,
+                                               const void* norm_weight_bf16, float eps,
+                                               const float* cos_sin, int64_t max_position,
+                                               const int64_t* positions, int32_t rope_neox,
+                                               const int64_t* slot_mapping, int64_t num_tokens,
+                                               uint8_t* kv_cache, int64_t num_blocks,
+                                               int32_t block_size, int64_t block_stride_bytes,
+                                               hipStream_t stream);
+
+/* Test export of the fused write path: out_f32 [num_tokens, 576] float32
+ * contiguous (16-byte aligned) receives, for every token, the binary32 values
+ * the fused path rounds to bf16: [normalised latent (512) | turned RoPE (64)],
+ * computed by the same device code; a position outside [0, max_position)
+ * gives NaN in that row's 64 RoPE values.  Arguments as for
+ * nvfp4_mla_norm_rope_quantize_append. */
+int nvfp4_mla_norm_rope_f32(const void* latent_bf16, int64_t latent_row_stride,
+                            const void* rope_bf16, int64_t rope_row_stride,
+                            const void* norm_weight_bf16, float eps, const float* cos_sin,
+                            int64_t max_position, const int64_t* positions, int32_t rope_neox,
+                            int64_t num_tokens, float* out_f32, hipStream_t stream);
 
 /*
  * Quantize-append into 432-byte "nvfp4_ds_mla" records (layout above): the
@@ -153,7 +228,7 @@ int nvfp4_mla_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row
                                      const int64_t* slot_mapping, int64_t num_tokens,
                                      uint8_t* kv_cache, int64_t num_blocks,
                                      int32_t block_size, int64_t block_stride_bytes,
-                                     void* stream);
+                                     hipStream_t stream);
 
 /*
  * Dequantize-gather: out[i, :] = the 576 bf16 values of the record at
@@ -166,7 +241,7 @@ int nvfp4_mla_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row
 int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks,
                                 int32_t block_size, int64_t block_stride_bytes,
                                 const int32_t* slots, int64_t n,
-                                void* out_bf16, void* stream);
+                                void* out_bf16, hipStream_t stream);
 
 /* Dequantize-gather over a cache of 432-byte records: NoPE as above, RoPE
  * the stored bf16 bits.  Arguments and errors as nvfp4_mla_dequantize_gather
@@ -174,12 +249,17 @@ int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks,
 int nvfp4_mla_dequantize_gather_ds_mla(const uint8_t* kv_cache, int64_t num_blocks,
                                        int32_t block_size, int64_t block_stride_bytes,
                                        const int32_t* slots, int64_t n,
-                                       void* out_bf16, void* stream);
+                                       void* out_bf16, hipStream_t stream);
 
 /*
  * Split planner.  Chooses the number of split-KV partitions for a decode of
  * this shape on the current device (deterministic, no calibration; the same
- * inputs always give the same answer on the same device model).
+ * inputs always give the same answer on the same device model).  The pages'
+ * decode paths pick their launch shape per problem shape in the same way:
+ * a planner memoised per shape that skips calibration while a stream is
+ * capturing (sglang PR #38646, Modifications, the attention branch) and a
+ * decode plan built ahead of the call (vLLM PR #82, Fix: the read path's
+ * plan construction).
  * Writes 1 <= *num_splits_out <= NVFP4_MLA_MAX_SPLITS.
  */
 int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q,
@@ -187,7 +267,10 @@ int nvfp4_mla_sparse_decode_plan(int32_t batch, int32_t s_q, int32_t h_q,
 
 /*
  * Workspace bytes a decode with num_splits partitions needs (0 when
- * num_splits == 1).  num_splits == 0 means "what the planner picks".
+ * num_splits == 1).  num_splits == 0 means "what the planner picks".  The
+ * caller allocates it once and keeps it for every later call, so that a
+ * call never allocates and can be captured into a graph (sglang PR #38646,
+ * Modifications: the graph-safe planner).
  * Returns 0 and sets the error on invalid arguments.
  *
  * The workspace holds the splits' partial O and LSE, which a combine kernel
@@ -227,7 +310,10 @@ size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
  * its head's largest magnitude; scores and sums are fp32; P enters PV as
  * fp16 hi + lo parts (about 2^-22 relative); O is rounded once to bf16 (with
  * splits, partial O is held in fp16 or fp32 first).  The results are the
- * same bits on every run and in graph replays.
+ * same bits on every run and in graph replays.  The waves of a workgroup
+ * wait for each other through bounded polls; a wait that ran out (correct
+ * execution never comes near the bound) makes that workgroup's rows and
+ * heads NaN in O and LSE rather than silently wrong.
  */
 int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int64_t num_blocks, int32_t block_size,
@@ -236,7 +322,7 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache,
                             int32_t topk, const float* attn_sink,
                             float softmax_scale, void* out_bf16, float* lse,
                             void* workspace, size_t workspace_bytes,
-                            int32_t num_splits, void* stream);
+                            int32_t num_splits, hipStream_t stream);
 
 /*
  * Allocation-free sparse decode, for callers that cannot allocate device
@@ -261,7 +347,7 @@ int nvfp4_mla_sparse_decode_noalloc(const void* q_bf16, const uint8_t* kv_cache,
                                     int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
                                     const float* attn_sink, float softmax_scale,
                                     void* out_bf16, float* lse, int32_t num_splits,
-                                    void* stream);
+                                    hipStream_t stream);
 
 /*
  * Sparse decode over a cache of 432-byte records: the attention of
@@ -277,7 +363,7 @@ int nvfp4_mla_sparse_decode_ds_mla(const void* q_bf16, const uint8_t* kv_cache,
                                    int32_t topk, const float* attn_sink,
                                    float softmax_scale, void* out_bf16, float* lse,
                                    void* workspace, size_t workspace_bytes,
-                                   int32_t num_splits, void* stream);
+                                   int32_t num_splits, hipStream_t stream);
 
 /*
  * Dual-cache sparse decode: the same attention as nvfp4_mla_sparse_decode,
@@ -316,7 +402,7 @@ int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache,
                                  const float* attn_sink, float softmax_scale,
                                  void* out_bf16, float* lse, void* workspace,
                                  size_t workspace_bytes, int32_t num_splits,
-                                 void* stream);
+                                 hipStream_t stream);
 
 /* Dual-cache sparse decode over two caches of 432-byte records: arguments
  * and errors as nvfp4_mla_sparse_decode_dual, both caches holding 432-byte
@@ -332,16 +418,20 @@ int nvfp4_mla_sparse_decode_dual_ds_mla(const void* q_bf16, const uint8_t* kv_ca
                                         const float* attn_sink, float softmax_scale,
                                         void* out_bf16, float* lse, void* workspace,
                                         size_t workspace_bytes, int32_t num_splits,
-                                        void* stream);
+                                        hipStream_t stream);
 
 /*
  * Split-KV combine.  Given num_splits sink-free partial results over
  * disjoint index subsets (O_i normalised within its subset, LSE_i natural
- * log; an empty subset has LSE_i = -inf):
+ * log; an empty subset has LSE_i = -inf) -- the merge a decode split over
+ * its top-k list, or over context-parallel ranks each holding part of the
+ * cache (vLLM PR #82 validates at TP4/DCP4, summary), needs to give the
+ * softmax of the whole list; the sink belongs to that whole softmax, so it is
+ * applied once here (FlashMLA PR #18, PR description: the attention sink):
  *     LSE = ln sum_i exp(LSE_i)
  *     O   = sum_i exp(LSE_i - LSE) O_i / (1 + exp(attn_sink[h] - LSE))
  * (sink factor only when attn_sink is non-NULL); all LSE_i = -inf gives
- * O = 0, LSE = -inf.
+ * O = 0, LSE = -inf, and a NaN LSE_i gives a NaN row.
  *   o_partial   [num_splits, rows, h_q, 512] float32 contiguous
  *   lse_partial [num_splits, rows, h_q] float32 contiguous
  *   out_bf16    [rows, h_q, 512] bf16;  lse [rows, h_q] float32
@@ -349,7 +439,7 @@ int nvfp4_mla_sparse_decode_dual_ds_mla(const void* q_bf16, const uint8_t* kv_ca
 int nvfp4_mla_combine(const float* o_partial, const float* lse_partial,
                       int32_t num_splits, int64_t rows, int32_t h_q,
                       const float* attn_sink, void* out_bf16, float* lse,
-                      void* stream);
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,14 @@ SIGNATURES = {
                                                     _I32, _P]),
     "nvfp4_mla_sparse_decode_noalloc": (ctypes.c_int, [_P, _P, _I64, _I32, _I64, _P, _I32, _I32,
                                                        _I32, _I32, _P, _F32, _P, _P, _I32, _P]),
+    "nvfp4_mla_norm_rope_quantize_append": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _F32, _P, _I64,
+                                                           _P, _I32, _P, _I64, _P, _I64, _I32,
+                                                           _I64, _P]),
+    "nvfp4_mla_norm_rope_quantize_append_ds_mla": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _F32, _P,
+                                                                  _I64, _P, _I32, _P, _I64, _P,
+                                                                  _I64, _I32, _I64, _P]),
+    "nvfp4_mla_norm_rope_f32": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _F32, _P, _I64, _P, _I32,
+                                               _I64, _P, _P]),
     "nvfp4_mla_quantize_append_ds_mla": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P,
                                                         _I64, _I32, _I64, _P]),
     "nvfp4_mla_dequantize_gather_ds_mla": (ctypes.c_int, [_P, _I64, _I32, _I64, _P, _I64, _P,
@@ -218,6 +226,67 @@ def quantize_append(latent, rope, slot_mapping, kv_cache):
         _ptr(kv_cache), nb, bs, stride, _stream(kv_cache.device))
     _check(fn, code)
     return kv_cache
+
+
+def _norm_rope_inputs(latent, rope, norm_weight, cos_sin, positions, device):
+    """Checks the fused write path's tensors; returns the token count."""
+    n = latent.shape[0]
+    if latent.dtype != torch.bfloat16 or rope.dtype != torch.bfloat16:
+        raise ValueError("latent and rope must be bfloat16")
+    if latent.dim() != 2 or rope.dim() != 2 or latent.shape[1] < NOPE_DIM or rope.shape[1] < ROPE_DIM:
+        raise ValueError("latent must be [N, >=512] and rope [N, >=64]")
+    if rope.shape[0] != n or latent.stride(-1) != 1 or rope.stride(-1) != 1:
+        raise ValueError("latent and rope need N rows with contiguous inner dimensions")
+    if (norm_weight.dtype != torch.bfloat16 or norm_weight.numel() != NOPE_DIM
+            or not norm_weight.is_contiguous()):
+        raise ValueError("norm_weight must be a contiguous bfloat16 [512] tensor")
+    if (cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM
+            or not cos_sin.is_contiguous()):
+        raise ValueError("cos_sin must be a contiguous float32 [max_position, 64] tensor")
+    if positions.dtype != torch.int64 or positions.numel() != n or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int64 [N] tensor")
+    _same_device(device, latent=latent, rope=rope, norm_weight=norm_weight, cos_sin=cos_sin,
+                 positions=positions)
+    return n
+
+
+def norm_rope_quantize_append(latent, rope, norm_weight, eps, cos_sin, positions, slot_mapping,
+                              kv_cache, neox=False):
+    """Fused write path, in place: RMSNorm(latent) * norm_weight and the
+    rotary turn of `rope` by the rows positions[n] of cos_sin ([max_position,
+    64] float32: 32 cosines, then 32 sines; pairs (2i, 2i+1), or (i, i+32)
+    when neox), both rounded to bf16, then quantized into the records at
+    slot_mapping.  Tokens with slot -1 or a position outside the table are
+    skipped."""
+    n = _norm_rope_inputs(latent, rope, norm_weight, cos_sin, positions, kv_cache.device)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 [N] tensor")
+    _same_device(kv_cache.device, slot_mapping=slot_mapping)
+    nb, bs, stride = _cache_geometry(kv_cache)
+    fn = "nvfp4_mla_norm_rope_quantize_append" + _ds(kv_cache)
+    code = getattr(lib(), fn)(
+        _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(norm_weight),
+        float(eps), _ptr(cos_sin), cos_sin.shape[0], _ptr(positions), int(bool(neox)),
+        _ptr(slot_mapping), n, _ptr(kv_cache), nb, bs, stride, _stream(kv_cache.device))
+    _check(fn, code)
+    return kv_cache
+
+
+def norm_rope_f32(latent, rope, norm_weight, eps, cos_sin, positions, neox=False, out=None):
+    """float32 [N, 576]: the fused path's normalised latent and turned RoPE
+    before their bf16 rounding (test export)."""
+    n = _norm_rope_inputs(latent, rope, norm_weight, cos_sin, positions, latent.device)
+    if out is None:
+        out = torch.empty((n, QK_DIM), dtype=torch.float32, device=latent.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (n, QK_DIM) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 [{n}, {QK_DIM}] tensor")
+    _same_device(latent.device, out=out)
+    code = lib().nvfp4_mla_norm_rope_f32(
+        _ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0), _ptr(norm_weight),
+        float(eps), _ptr(cos_sin), cos_sin.shape[0], _ptr(positions), int(bool(neox)), n,
+        _ptr(out), _stream(latent.device))
+    _check("nvfp4_mla_norm_rope_f32", code)
+    return out
 
 
 def dequantize_gather(kv_cache, slots, out=None):

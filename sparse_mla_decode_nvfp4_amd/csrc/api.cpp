@@ -225,7 +225,8 @@ int quantize_append_impl(const char* fn, const void* latent_bf16, int64_t latent
                          const void* rope_bf16, int64_t rope_row_stride,
                          const int64_t* slot_mapping, int64_t num_tokens, uint8_t* kv_cache,
                          int64_t num_blocks, int32_t block_size, int64_t block_stride_bytes,
-                         bool f16_input, int32_t record_bytes, void* stream) {
+                         bool f16_input, int32_t record_bytes, hipStream_t stream,
+                         const nvfp4::NormRope* fused = nullptr) {
   if (num_tokens < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
   int64_t num_slots = 0;
   int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots,
@@ -248,14 +249,50 @@ int quantize_append_impl(const char* fn, const void* latent_bf16, int64_t latent
   }
   rc = check_device(nullptr);
   if (rc) return rc;
-  hipError_t e = nvfp4::launch_quantize_append(
-      static_cast<const uint16_t*>(latent_bf16), latent_row_stride,
-      static_cast<const uint16_t*>(rope_bf16), rope_row_stride, slot_mapping, num_tokens, kv_cache,
-      num_slots, make_page_addr(block_size, block_stride_bytes, record_bytes), f16_input,
-      static_cast<hipStream_t>(stream));
+  const nvfp4::PageAddr pa = make_page_addr(block_size, block_stride_bytes, record_bytes);
+  hipError_t e =
+      fused ? nvfp4::launch_norm_rope_quantize_append(
+                  static_cast<const uint16_t*>(latent_bf16), latent_row_stride,
+                  static_cast<const uint16_t*>(rope_bf16), rope_row_stride, *fused, slot_mapping,
+                  num_tokens, kv_cache, num_slots, pa, stream)
+            : nvfp4::launch_quantize_append(
+                  static_cast<const uint16_t*>(latent_bf16), latent_row_stride,
+                  static_cast<const uint16_t*>(rope_bf16), rope_row_stride, slot_mapping,
+                  num_tokens, kv_cache, num_slots, pa, f16_input, stream);
   if (e != hipSuccess)
     return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+// Checks the fused prologue's arguments (needed only when tokens are
+// written) and fills `nr`.
+int check_norm_rope(const void* norm_weight_bf16, float eps, const float* cos_sin,
+                    int64_t max_position, const int64_t* positions, int32_t rope_neox,
+                    int64_t num_tokens, nvfp4::NormRope* nr) {
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (rope_neox != 0 && rope_neox != 1)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "rope_neox must be 0 (pairs 2i, 2i+1) or 1 "
+                "(pairs i, i+32)");
+  if (max_position < 1)
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "max_position must be >= 1");
+  if (max_position > (INT64_MAX / 256))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "max_position too large");
+  if (num_tokens > 0) {
+    if (!norm_weight_bf16 || !cos_sin || !positions)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "norm_weight, cos_sin and positions must be non-NULL");
+    if (!aligned(norm_weight_bf16, 16) || !aligned(cos_sin, 4) || !aligned(positions, 8))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "norm_weight must be 16-byte aligned, cos_sin 4-byte and positions 8-byte");
+  }
+  nr->weight = static_cast<const uint16_t*>(norm_weight_bf16);
+  nr->eps = eps;
+  nr->cos_sin = cos_sin;
+  nr->max_position = max_position;
+  nr->positions = positions;
+  nr->neox = rope_neox;
+  return NVFP4_MLA_OK;
 }
 
 // Shared by the single- and dual-cache exports.  `extra` is null for the
@@ -276,7 +313,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
                        int32_t batch, int32_t s_q, int32_t h_q, const float* attn_sink,
                        float softmax_scale, void* out_bf16, float* lse, void* workspace,
                        size_t workspace_bytes_in, int32_t num_splits, int32_t record_bytes,
-                       void* stream, bool static_scratch = false) {
+                       hipStream_t stream, bool static_scratch = false) {
   if (extra && (topk0 < 0 || extra->topk < 0 || topk0 > 65536 || extra->topk > 65536))
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "topk = %d and extra_topk = %d must be in [0, 65536]",
                 topk0, extra ? extra->topk : 0);
@@ -364,7 +401,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
     a.o_part = reinterpret_cast<float*>(base + w.o_off);
     a.lse_part = reinterpret_cast<float*>(base + w.lse_off);
   }
-  hipError_t e = nvfp4::launch_decode(a, static_cast<hipStream_t>(stream));
+  hipError_t e = nvfp4::launch_decode(a, stream);
   if (e != hipSuccess)
     return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -372,7 +409,7 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
 
 int dequantize_gather_impl(const char* fn, const uint8_t* kv_cache, int64_t num_blocks,
                            int32_t block_size, int64_t block_stride_bytes, const int32_t* slots,
-                           int64_t n, void* out_bf16, int32_t record_bytes, void* stream) {
+                           int64_t n, void* out_bf16, int32_t record_bytes, hipStream_t stream) {
   if (n < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "n must be >= 0");
   int64_t num_slots = 0;
   int rc = check_cache(kv_cache, num_blocks, block_size, block_stride_bytes, &num_slots,
@@ -393,7 +430,7 @@ int dequantize_gather_impl(const char* fn, const uint8_t* kv_cache, int64_t num_
                                                  make_page_addr(block_size, block_stride_bytes,
                                                                 record_bytes),
                                                  slots, n, static_cast<uint16_t*>(out_bf16),
-                                                 static_cast<hipStream_t>(stream));
+                                                 stream);
   if (e != hipSuccess)
     return fail(NVFP4_MLA_ERR_HIP, "%s launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -423,7 +460,7 @@ int nvfp4_mla_quantize_append(const void* latent_bf16, int64_t latent_row_stride
                               const void* rope_bf16, int64_t rope_row_stride,
                               const int64_t* slot_mapping, int64_t num_tokens,
                               uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                              int64_t block_stride_bytes, void* stream) {
+                              int64_t block_stride_bytes, hipStream_t stream) {
   return quantize_append_impl("quantize_append", latent_bf16, latent_row_stride, rope_bf16,
                               rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
                               block_size, block_stride_bytes, false, NVFP4_MLA_RECORD_BYTES,
@@ -434,7 +471,7 @@ int nvfp4_mla_quantize_append_ds_mla(const void* latent_bf16, int64_t latent_row
                                      const void* rope_bf16, int64_t rope_row_stride,
                                      const int64_t* slot_mapping, int64_t num_tokens,
                                      uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                                     int64_t block_stride_bytes, void* stream) {
+                                     int64_t block_stride_bytes, hipStream_t stream) {
   return quantize_append_impl("quantize_append_ds_mla", latent_bf16, latent_row_stride,
                               rope_bf16, rope_row_stride, slot_mapping, num_tokens, kv_cache,
                               num_blocks, block_size, block_stride_bytes, false,
@@ -445,16 +482,83 @@ int nvfp4_mla_quantize_append_fp16(const void* latent_fp16, int64_t latent_row_s
                                    const void* rope_fp16, int64_t rope_row_stride,
                                    const int64_t* slot_mapping, int64_t num_tokens,
                                    uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                                   int64_t block_stride_bytes, void* stream) {
+                                   int64_t block_stride_bytes, hipStream_t stream) {
   return quantize_append_impl("quantize_append_fp16", latent_fp16, latent_row_stride, rope_fp16,
                               rope_row_stride, slot_mapping, num_tokens, kv_cache, num_blocks,
                               block_size, block_stride_bytes, true, NVFP4_MLA_RECORD_BYTES,
                               stream);
 }
 
+int nvfp4_mla_norm_rope_quantize_append(
+    const void* latent_bf16, int64_t latent_row_stride, const void* rope_bf16,
+    int64_t rope_row_stride, const void* norm_weight_bf16, float eps, const float* cos_sin,
+    int64_t max_position, const int64_t* positions, int32_t rope_neox,
+    const int64_t* slot_mapping, int64_t num_tokens, uint8_t* kv_cache, int64_t num_blocks,
+    int32_t block_size, int64_t block_stride_bytes, hipStream_t stream) {
+  nvfp4::NormRope nr{};
+  int rc = check_norm_rope(norm_weight_bf16, eps, cos_sin, max_position, positions, rope_neox,
+                           num_tokens, &nr);
+  if (rc) return rc;
+  return quantize_append_impl("norm_rope_quantize_append", latent_bf16, latent_row_stride,
+                              rope_bf16, rope_row_stride, slot_mapping, num_tokens, kv_cache,
+                              num_blocks, block_size, block_stride_bytes, false,
+                              NVFP4_MLA_RECORD_BYTES, stream, &nr);
+}
+
+int nvfp4_mla_norm_rope_quantize_append_ds_mla(
+    const void* latent_bf16, int64_t latent_row_stride, const void* rope_bf16,
+    int64_t rope_row_stride, const void* norm_weight_bf16, float eps, const float* cos_sin,
+    int64_t max_position, const int64_t* positions, int32_t rope_neox,
+    const int64_t* slot_mapping, int64_t num_tokens, uint8_t* kv_cache, int64_t num_blocks,
+    int32_t block_size, int64_t block_stride_bytes, hipStream_t stream) {
+  nvfp4::NormRope nr{};
+  int rc = check_norm_rope(norm_weight_bf16, eps, cos_sin, max_position, positions, rope_neox,
+                           num_tokens, &nr);
+  if (rc) return rc;
+  return quantize_append_impl("norm_rope_quantize_append_ds_mla", latent_bf16, latent_row_stride,
+                              rope_bf16, rope_row_stride, slot_mapping, num_tokens, kv_cache,
+                              num_blocks, block_size, block_stride_bytes, false,
+                              NVFP4_MLA_DS_MLA_RECORD_BYTES, stream, &nr);
+}
+
+int nvfp4_mla_norm_rope_f32(const void* latent_bf16, int64_t latent_row_stride,
+                            const void* rope_bf16, int64_t rope_row_stride,
+                            const void* norm_weight_bf16, float eps, const float* cos_sin,
+                            int64_t max_position, const int64_t* positions, int32_t rope_neox,
+                            int64_t num_tokens, float* out_f32, hipStream_t stream) {
+  if (num_tokens < 0) return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  nvfp4::NormRope nr{};
+  int rc = check_norm_rope(norm_weight_bf16, eps, cos_sin, max_position, positions, rope_neox,
+                           num_tokens, &nr);
+  if (rc) return rc;
+  if (num_tokens > 0) {
+    if (!latent_bf16 || !rope_bf16 || !out_f32)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "latent, rope and out must be non-NULL");
+    if (latent_row_stride < NVFP4_MLA_NOPE_DIM || rope_row_stride < NVFP4_MLA_ROPE_DIM)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "row strides (%lld, %lld) must be >= (512, 64) elements",
+                  (long long)latent_row_stride, (long long)rope_row_stride);
+    if (!aligned(latent_bf16, 16) || latent_row_stride % 8 != 0 || !aligned(rope_bf16, 2) ||
+        !aligned(out_f32, 16))
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                  "latent rows and out must be 16-byte aligned, rope 2-byte aligned");
+    if (num_tokens > (int64_t)0x7FFFFFFF * 4)
+      return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_tokens too large");
+  }
+  rc = check_device(nullptr);
+  if (rc) return rc;
+  hipError_t e = nvfp4::launch_norm_rope_f32(static_cast<const uint16_t*>(latent_bf16),
+                                             latent_row_stride,
+                                             static_cast<const uint16_t*>(rope_bf16),
+                                             rope_row_stride, nr, num_tokens, out_f32, stream);
+  if (e != hipSuccess)
+    return fail(NVFP4_MLA_ERR_HIP, "norm_rope_f32 launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
                                 int64_t block_stride_bytes, const int32_t* slots, int64_t n,
-                                void* out_bf16, void* stream) {
+                                void* out_bf16, hipStream_t stream) {
   return dequantize_gather_impl("dequantize_gather", kv_cache, num_blocks, block_size,
                                 block_stride_bytes, slots, n, out_bf16, NVFP4_MLA_RECORD_BYTES,
                                 stream);
@@ -463,7 +567,7 @@ int nvfp4_mla_dequantize_gather(const uint8_t* kv_cache, int64_t num_blocks, int
 int nvfp4_mla_dequantize_gather_ds_mla(const uint8_t* kv_cache, int64_t num_blocks,
                                        int32_t block_size, int64_t block_stride_bytes,
                                        const int32_t* slots, int64_t n, void* out_bf16,
-                                       void* stream) {
+                                       hipStream_t stream) {
   return dequantize_gather_impl("dequantize_gather_ds_mla", kv_cache, num_blocks, block_size,
                                 block_stride_bytes, slots, n, out_bf16,
                                 NVFP4_MLA_DS_MLA_RECORD_BYTES, stream);
@@ -504,7 +608,7 @@ int nvfp4_mla_sparse_decode(const void* q_bf16, const uint8_t* kv_cache, int64_t
                             const int32_t* indices, int32_t batch, int32_t s_q, int32_t h_q,
                             int32_t topk, const float* attn_sink, float softmax_scale,
                             void* out_bf16, float* lse, void* workspace, size_t workspace_bytes_in,
-                            int32_t num_splits, void* stream) {
+                            int32_t num_splits, hipStream_t stream) {
   return sparse_decode_impl("sparse_decode", q_bf16, kv_cache, num_blocks, block_size,
                             block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
                             attn_sink, softmax_scale, out_bf16, lse, workspace,
@@ -516,7 +620,7 @@ int nvfp4_mla_sparse_decode_noalloc(const void* q_bf16, const uint8_t* kv_cache,
                                     int64_t block_stride_bytes, const int32_t* indices,
                                     int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
                                     const float* attn_sink, float softmax_scale, void* out_bf16,
-                                    float* lse, int32_t num_splits, void* stream) {
+                                    float* lse, int32_t num_splits, hipStream_t stream) {
   return sparse_decode_impl("sparse_decode_noalloc", q_bf16, kv_cache, num_blocks, block_size,
                             block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
                             attn_sink, softmax_scale, out_bf16, lse, nullptr, 0, num_splits,
@@ -529,7 +633,7 @@ int nvfp4_mla_sparse_decode_ds_mla(const void* q_bf16, const uint8_t* kv_cache,
                                    int32_t batch, int32_t s_q, int32_t h_q, int32_t topk,
                                    const float* attn_sink, float softmax_scale, void* out_bf16,
                                    float* lse, void* workspace, size_t workspace_bytes_in,
-                                   int32_t num_splits, void* stream) {
+                                   int32_t num_splits, hipStream_t stream) {
   return sparse_decode_impl("sparse_decode_ds_mla", q_bf16, kv_cache, num_blocks, block_size,
                             block_stride_bytes, indices, topk, nullptr, batch, s_q, h_q,
                             attn_sink, softmax_scale, out_bf16, lse, workspace,
@@ -546,7 +650,7 @@ int nvfp4_mla_sparse_decode_dual(const void* q_bf16, const uint8_t* kv_cache, in
                                  int32_t s_q, int32_t h_q, const float* attn_sink,
                                  float softmax_scale, void* out_bf16, float* lse,
                                  void* workspace, size_t workspace_bytes_in, int32_t num_splits,
-                                 void* stream) {
+                                 hipStream_t stream) {
   const ExtraCache extra{extra_kv_cache, extra_num_blocks, extra_block_size,
                          extra_block_stride_bytes, extra_indices, extra_topk};
   return sparse_decode_impl("sparse_decode_dual", q_bf16, kv_cache, num_blocks, block_size,
@@ -562,7 +666,7 @@ int nvfp4_mla_sparse_decode_dual_ds_mla(
     int64_t extra_block_stride_bytes, const int32_t* extra_indices, int32_t extra_topk,
     int32_t batch, int32_t s_q, int32_t h_q, const float* attn_sink, float softmax_scale,
     void* out_bf16, float* lse, void* workspace, size_t workspace_bytes_in, int32_t num_splits,
-    void* stream) {
+    hipStream_t stream) {
   const ExtraCache extra{extra_kv_cache, extra_num_blocks, extra_block_size,
                          extra_block_stride_bytes, extra_indices, extra_topk};
   return sparse_decode_impl("sparse_decode_dual_ds_mla", q_bf16, kv_cache, num_blocks,
@@ -574,7 +678,7 @@ int nvfp4_mla_sparse_decode_dual_ds_mla(
 
 int nvfp4_mla_combine(const float* o_partial, const float* lse_partial, int32_t num_splits,
                       int64_t rows, int32_t h_q, const float* attn_sink, void* out_bf16,
-                      float* lse, void* stream) {
+                      float* lse, hipStream_t stream) {
   if (num_splits < 1 || num_splits > 4096)
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d must be in [1, 4096]", num_splits);
   if (rows < 0 || h_q < 1)
@@ -592,7 +696,7 @@ int nvfp4_mla_combine(const float* o_partial, const float* lse_partial, int32_t 
   if (rc) return rc;
   hipError_t e = nvfp4::launch_combine(o_partial, lse_partial, num_splits, rows, h_q, attn_sink,
                                        static_cast<uint16_t*>(out_bf16), lse,
-                                       static_cast<hipStream_t>(stream));
+                                       stream);
   if (e != hipSuccess)
     return fail(NVFP4_MLA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -65,6 +65,58 @@ __device__ __forceinline__ float widen16(uint32_t bits16) {
   else return __uint_as_float(bits16 << 16);
 }
 
+// ---- the fused prologue: RMSNorm and rotary turn in binary32, each step
+// rounded to nearest even (no fused multiply-add), then bf16 rounding.  The
+// sum of squares has a fixed order: lane l adds the squares of its elements
+// 8l..8l+7 in element order, then the 64 partial sums meet in a butterfly
+// (neighbours first), which leaves every lane the same total.
+
+// bf16 value nearest to a finite fp32 value (ties to even), as fp32.
+__device__ __forceinline__ float round_bf16(float y) {
+  uint32_t u = __float_as_uint(y);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// x[8] (elements 8l..8l+7 of one token's latent) <- x * w / sqrt(mean(x^2) + eps),
+// before rounding.  Every lane of the wave takes part (the butterfly).
+__device__ __forceinline__ void rms_norm8(float (&x)[8], const float (&w)[8], float eps) {
+#pragma clang fp contract(off)
+  float p = x[0] * x[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) p = p + x[i] * x[i];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) p = p + __shfl_xor(p, d);
+  const float v = p * (1.0f / 512.0f) + eps;          // the scaling is exact
+  const float r = 1.0f / __builtin_sqrtf(v);          // IEEE sqrt, IEEE divide
+#pragma unroll
+  for (int i = 0; i < 8; i++) x[i] = (x[i] * r) * w[i];
+}
+
+// One element of a rotated pair: a*c - b*s for the first element (xl = a,
+// xp = b), b*c + a*s for the second (xl = b, xp = a).
+__device__ __forceinline__ float rotate1(float xl, float xp, float c, float s, bool first) {
+#pragma clang fp contract(off)
+  const float u = xl * c;
+  const float t = xp * s;
+  return first ? u - t : u + t;
+}
+
+// Lane l's RoPE element after the turn for a token at `pos` (the table row is
+// read only for a position inside the table; others give NaN).  The pair
+// partner is lane l^1 (interleaved) or l^32 (neox); its frequency l>>1 or
+// l&31.  Every lane of the wave takes part (the partner exchange).
+__device__ __forceinline__ float rope_turn(float xl, int64_t pos, const NormRope& nr, int lane) {
+  const int partner = nr.neox ? (lane ^ 32) : (lane ^ 1);
+  const int freq = nr.neox ? (lane & 31) : (lane >> 1);
+  const bool first = nr.neox ? lane < 32 : (lane & 1) == 0;
+  const float xp = __shfl(xl, partner);
+  const bool in_table = pos >= 0 && pos < nr.max_position;
+  const float* row = nr.cos_sin + (in_table ? pos : 0) * 64;
+  const float r = rotate1(xl, xp, row[freq], row[32 + freq], first);
+  return in_table ? r : __builtin_nanf("");
+}
+
 // One wavefront per kTokW consecutive tokens; 4 waves per 256-thread block.
 // Lane l quantizes NoPE elements [8l, 8l+8) (block l/2) and RoPE element l;
 // each record is assembled in LDS and written with 16-byte stores (22 or 27).
@@ -72,13 +124,18 @@ __device__ __forceinline__ float widen16(uint32_t bits16) {
 // bf16 value is exact in fp32, so the rounding below is the same for both.
 constexpr int kTokW = 4;
 
-template <bool kF16, class F>
+// With kFused the tokens first go through the norm + rotary prologue and
+// are rounded to bf16 (bf16 inputs only); a token whose position lies outside
+// the table is skipped like an unmapped one.
+template <bool kF16, class F, bool kFused = false>
 __global__ void __launch_bounds__(256)
 quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
                        const uint16_t* __restrict__ rope, int64_t rstride,
                        const int64_t* __restrict__ slot_mapping, int64_t num_tokens,
-                       uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa) {
+                       uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa,
+                       NormRope nr) {
   static_assert(!(kF16 && F::kBf16Rope), "the 432-byte record holds bf16 RoPE");
+  static_assert(!(kF16 && kFused), "the fused path takes bf16 inputs");
   __shared__ __attribute__((aligned(16))) uint8_t rec[4][F::kBytes];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -90,23 +147,42 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
   int64_t slot[kTokW];
   u32x4 raw[kTokW];
   uint32_t rbits[kTokW];
+  int64_t pos[kTokW];
 #pragma unroll
   for (int t = 0; t < kTokW; t++) {
     const int64_t tok = min(tok0 + t, num_tokens - 1);
     slot[t] = tok0 + t < num_tokens ? slot_mapping[tok] : -1;
     raw[t] = *reinterpret_cast<const u32x4*>(latent + tok * lstride + 8 * lane);
     rbits[t] = (uint32_t)rope[tok * rstride + lane];
+    if constexpr (kFused) pos[t] = nr.positions[tok];
+  }
+  float wgt[8];
+  if constexpr (kFused) {
+    const u32x4 wr = *reinterpret_cast<const u32x4*>(nr.weight + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      wgt[2 * i] = __uint_as_float(wr[i] << 16);
+      wgt[2 * i + 1] = __uint_as_float(wr[i] & 0xFFFF0000u);
+    }
   }
   uint8_t* r = rec[wave];
 #pragma unroll
   for (int t = 0; t < kTokW; t++) {
-    const bool mapped = slot[t] >= 0 && slot[t] < num_slots;   // uniform over the wave
+    bool mapped = slot[t] >= 0 && slot[t] < num_slots;   // uniform over the wave
     // ---- NoPE: 8 elements per lane, two lanes per 16-element block
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       x[2 * i] = widen16<kF16>(raw[t][i] & 0xFFFFu);
       x[2 * i + 1] = widen16<kF16>(raw[t][i] >> 16);
+    }
+    float rv = widen16<kF16>(rbits[t]);
+    if constexpr (kFused) {
+      rms_norm8(x, wgt, nr.eps);
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = round_bf16(x[i]);
+      rv = round_bf16(rope_turn(rv, pos[t], nr, lane));
+      mapped = mapped && pos[t] >= 0 && pos[t] < nr.max_position;
     }
     float amax = 0.0f;
 #pragma unroll
@@ -126,10 +202,11 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
     if ((lane & 1) == 0) r[F::scale_at(lane >> 1)] = (uint8_t)scode;
     // ---- RoPE: lane l handles element l
     if constexpr (F::kBf16Rope) {
-      reinterpret_cast<uint16_t*>(r + F::kRopeOff)[lane] = (uint16_t)rbits[t];   // verbatim
+      // verbatim bf16 (the rounded turn in the fused path)
+      reinterpret_cast<uint16_t*>(r + F::kRopeOff)[lane] =
+          kFused ? (uint16_t)(__float_as_uint(rv) >> 16) : (uint16_t)rbits[t];
       if (lane < 4) reinterpret_cast<uint32_t*>(r + F::kPadOff)[lane] = 0u;
     } else {
-      const float rv = widen16<kF16>(rbits[t]);
       const uint32_t rcode = e4m3_rne_sat_mag(fabsf(rv)) | ((__float_as_uint(rv) >> 24) & 0x80u);
       r[F::kRopeOff + lane] = (uint8_t)rcode;
     }
@@ -193,16 +270,74 @@ hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
     if (f16_input) return hipErrorInvalidValue;    // rejected by the caller already
     hipLaunchKernelGGL((quantize_append_kernel<false, Fmt432>), grid, dim3(256), 0, stream,
                        latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
-                       num_slots, pa);
+                       num_slots, pa, NormRope{});
   } else if (f16_input) {
     hipLaunchKernelGGL((quantize_append_kernel<true, Fmt352>), grid, dim3(256), 0, stream,
                        latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
-                       num_slots, pa);
+                       num_slots, pa, NormRope{});
   } else {
     hipLaunchKernelGGL((quantize_append_kernel<false, Fmt352>), grid, dim3(256), 0, stream,
                        latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
-                       num_slots, pa);
+                       num_slots, pa, NormRope{});
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_rope_quantize_append(const uint16_t* latent, int64_t lstride,
+                                            const uint16_t* rope, int64_t rstride,
+                                            const NormRope& nr, const int64_t* slot_mapping,
+                                            int64_t num_tokens, uint8_t* cache,
+                                            int64_t num_slots, const PageAddr& pa,
+                                            hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((num_tokens + 4 * kTokW - 1) / (4 * kTokW)));
+  if (pa.record_bytes == Fmt432::kBytes)
+    hipLaunchKernelGGL((quantize_append_kernel<false, Fmt432, true>), grid, dim3(256), 0, stream,
+                       latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
+                       num_slots, pa, nr);
+  else
+    hipLaunchKernelGGL((quantize_append_kernel<false, Fmt352, true>), grid, dim3(256), 0, stream,
+                       latent, lstride, rope, rstride, slot_mapping, num_tokens, cache,
+                       num_slots, pa, nr);
+  return hipGetLastError();
+}
+
+// One wavefront per token: the fused prologue's fp32 results before their
+// bf16 rounding (lane l: latent elements 8l..8l+7, RoPE element l).
+__global__ void __launch_bounds__(256)
+norm_rope_f32_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
+                     const uint16_t* __restrict__ rope, int64_t rstride, NormRope nr,
+                     int64_t num_tokens, float* __restrict__ out) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
+  if (tok >= num_tokens) return;
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(latent + tok * lstride + 8 * lane);
+  const u32x4 wr = *reinterpret_cast<const u32x4*>(nr.weight + 8 * lane);
+  float x[8], w[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = __uint_as_float(raw[i] << 16);
+    x[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+    w[2 * i] = __uint_as_float(wr[i] << 16);
+    w[2 * i + 1] = __uint_as_float(wr[i] & 0xFFFF0000u);
+  }
+  rms_norm8(x, w, nr.eps);
+  const float rv = __uint_as_float((uint32_t)rope[tok * rstride + lane] << 16);
+  const float turned = rope_turn(rv, nr.positions[tok], nr, lane);
+  float* o = out + tok * kQkDim;
+  reinterpret_cast<f32x4*>(o + 8 * lane)[0] = f32x4{x[0], x[1], x[2], x[3]};
+  reinterpret_cast<f32x4*>(o + 8 * lane)[1] = f32x4{x[4], x[5], x[6], x[7]};
+  o[kNopeDim + lane] = turned;
+}
+
+hipError_t launch_norm_rope_f32(const uint16_t* latent, int64_t lstride, const uint16_t* rope,
+                                int64_t rstride, const NormRope& nr, int64_t num_tokens,
+                                float* out, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const dim3 grid((uint32_t)((num_tokens + 3) / 4));
+  hipLaunchKernelGGL(norm_rope_f32_kernel, grid, dim3(256), 0, stream, latent, lstride, rope,
+                     rstride, nr, num_tokens, out);
   return hipGetLastError();
 }
 

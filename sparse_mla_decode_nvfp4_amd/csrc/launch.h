@@ -15,6 +15,31 @@ hipError_t launch_quantize_append(const uint16_t* latent, int64_t lstride,
                                   uint8_t* cache, int64_t num_slots, const PageAddr& pa,
                                   bool f16_input, hipStream_t stream);
 
+// The fused write path's prologue: RMSNorm of the latent and the rotary
+// turn of the RoPE part, both rounded to bf16 before the write rule.
+struct NormRope {
+  const uint16_t* weight;   // [512] bf16 RMSNorm weight
+  float eps;
+  const float* cos_sin;     // [max_position, 64] fp32: cos of the 32 frequencies, then sin
+  int64_t max_position;
+  const int64_t* positions; // [num_tokens]
+  int32_t neox;             // 1: pairs (i, i+32); 0: pairs (2i, 2i+1)
+};
+
+// Quantize-append of normalised and rotated bf16 inputs (one pass).
+hipError_t launch_norm_rope_quantize_append(const uint16_t* latent, int64_t lstride,
+                                            const uint16_t* rope, int64_t rstride,
+                                            const NormRope& nr, const int64_t* slot_mapping,
+                                            int64_t num_tokens, uint8_t* cache,
+                                            int64_t num_slots, const PageAddr& pa,
+                                            hipStream_t stream);
+
+// The fused path's fp32 values before their bf16 rounding: out [n, 576] =
+// [normalised latent (512) | rotated RoPE (64)] (test export).
+hipError_t launch_norm_rope_f32(const uint16_t* latent, int64_t lstride, const uint16_t* rope,
+                                int64_t rstride, const NormRope& nr, int64_t num_tokens,
+                                float* out, hipStream_t stream);
+
 hipError_t launch_dequantize_gather(const uint8_t* cache, int64_t num_slots, const PageAddr& pa,
                                     const int32_t* slots, int64_t n, uint16_t* out,
                                     hipStream_t stream);

@@ -9,7 +9,7 @@ Every draw comes from numpy's PCG64 seeded as default_rng([config, stream,
 rep]) with one stream per kind of input:
   0 channel scales, 1 NoPE latents, 2 RoPE latents, 3 queries,
   4 indices + invalid mask, 5 sinks, 6 page tables / lengths,
-  7 sentinel cache bytes, 8 slot mapping.
+  7 sentinel cache bytes, 8 slot mapping, 9 norm weights and positions.
 
 Value distributions (the same for every workload):
   NoPE  = N(0,1) * channel_scale[d], channel_scale ~ exp(U(ln 0.1, ln 4)) fixed
@@ -270,6 +270,37 @@ def append_write(rep=0, num_tokens=16384, num_slots=262144, p_skip=0.10):
                                           dtype=np.uint8)
     return AppendWorkload("append_write", num_tokens, bs, num_slots // bs,
                           latent, rope, sm, sentinel)
+
+
+@dataclass
+class NormRopeInputs:
+    """The fused write path's extra inputs: an RMSNorm weight, a rotary table
+    and each token's position."""
+    norm_weight: torch.Tensor            # bf16 [512]
+    eps: float
+    cos_sin: torch.Tensor                # float32 [max_position, 64]: cos, then sin
+    positions: np.ndarray                # int64 [num_tokens]
+
+
+def rotary_table(max_position, base=10000.0):
+    """The usual rotary angles pos * base^(-2i/64) for the 32 frequencies,
+    as a float32 table [max_position, 64] of their cosines then sines (an
+    input of the fused write path, drawn here the way models build it)."""
+    inv = base ** (-np.arange(0, 64, 2, dtype=np.float64) / 64.0)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32))
+
+
+def norm_rope_inputs(num_tokens, rep=0, max_position=8192, eps=1e-6, p_outside=0.0):
+    """Seeded fused-path inputs for num_tokens tokens (config 3's stream 9):
+    weight ~ U(0.5, 1.5) in bf16, positions uniform in [0, max_position),
+    a fraction p_outside of them moved just outside the table."""
+    r = _rng(3, 9, rep)
+    weight = _bf16(r.uniform(0.5, 1.5, NOPE_DIM))
+    pos = r.integers(0, max_position, size=num_tokens).astype(np.int64)
+    out = r.random(num_tokens) < p_outside
+    pos[out] = np.where(r.random(int(out.sum())) < 0.5, -1, max_position)
+    return NormRopeInputs(weight, float(np.float32(eps)), rotary_table(max_position), pos)
 
 
 @dataclass

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = m.lib()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
         assert name in m.SIGNATURES, name
@@ -165,6 +165,82 @@ def test_sparse_decode_noalloc_without_a_gpu_reports_the_device_gate():
         pytest.skip("device-gate check is for GPU-less hosts")
     assert dec_noalloc() == m.ERR_UNSUPPORTED_DEVICE
     assert dec_noalloc(splits=4) == m.ERR_UNSUPPORTED_DEVICE
+
+
+def fused(fn="nvfp4_mla_norm_rope_quantize_append", **kw):
+    rb = 432 if fn.endswith("ds_mla") else 352
+    a = dict(latent=P16, lstride=512, rope=P16, rstride=64, weight=P16, eps=1e-6, cs=P16,
+             maxpos=128, pos=P16, neox=0, slots=P16, n=4, cache=P16, nblocks=4, bs=64,
+             stride=64 * rb, stream=NULL)
+    a.update(kw)
+    return getattr(m.lib(), fn)(a["latent"], a["lstride"], a["rope"], a["rstride"], a["weight"],
+                                a["eps"], a["cs"], a["maxpos"], a["pos"], a["neox"], a["slots"],
+                                a["n"], a["cache"], a["nblocks"], a["bs"], a["stride"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["nvfp4_mla_norm_rope_quantize_append",
+                                "nvfp4_mla_norm_rope_quantize_append_ds_mla"])
+@pytest.mark.parametrize("kw, needle", [
+    (dict(eps=float("nan")), "eps"),
+    (dict(eps=-1e-6), "eps"),
+    (dict(eps=float("inf")), "eps"),
+    (dict(neox=2), "rope_neox"),
+    (dict(maxpos=0), "max_position"),
+    (dict(weight=NULL), "non-NULL"),
+    (dict(cs=NULL), "non-NULL"),
+    (dict(pos=NULL), "non-NULL"),
+    (dict(weight=ctypes.c_void_p(0x100008)), "aligned"),
+    (dict(pos=ctypes.c_void_p(0x100004)), "aligned"),
+    (dict(lstride=500), "row strides"),
+    (dict(cache=NULL), "kv_cache"),
+    (dict(stride=64 * 352 - 16), "block_size"),
+])
+def test_fused_write_rejects_bad_arguments(fn, kw, needle):
+    if fn.endswith("ds_mla") and kw.get("stride") == 64 * 352 - 16:
+        kw = dict(stride=64 * 432 - 16)
+    assert fused(fn, **kw) == m.ERR_INVALID_ARGUMENT
+    assert needle in m.last_error()
+
+
+def test_fused_f32_export_rejects_bad_arguments():
+    lib = m.lib()
+    call = lambda **kw: lib.nvfp4_mla_norm_rope_f32(
+        kw.get("latent", P16), 512, P16, 64, kw.get("weight", P16), kw.get("eps", 0.0), P16,
+        kw.get("maxpos", 16), P16, 0, kw.get("n", 3), kw.get("out", P16), NULL)
+    assert call(n=-1) == m.ERR_INVALID_ARGUMENT
+    assert call(eps=float("nan")) == m.ERR_INVALID_ARGUMENT
+    assert call(out=NULL) == m.ERR_INVALID_ARGUMENT
+    assert call(out=ctypes.c_void_p(0x100004)) == m.ERR_INVALID_ARGUMENT
+    assert "aligned" in m.last_error()
+    assert call(maxpos=0) == m.ERR_INVALID_ARGUMENT
+
+
+def test_header_compiles_as_c_and_cxx():
+    """The header is plain C (its own hipStream_t declaration, no HIP
+    include needed) and sits beside hip_runtime_api.h in C++."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc, cxx = shutil.which("gcc"), shutil.which("g++")
+    if cc is None or cxx is None:
+        pytest.skip("no host compiler")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        with open(c, "w") as f:
+            f.write('#include "nvfp4_mla.h"\nint main(void) { hipStream_t s = 0; (void)s; '
+                    'int (*f)(void) = nvfp4_mla_abi_version; return f == 0; }\n')
+        r = subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-I",
+                            os.path.dirname(HEADER), c], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        cpp = os.path.join(d, "t.cpp")
+        with open(cpp, "w") as f:
+            f.write('#include "nvfp4_mla.h"\n#include <hip/hip_runtime_api.h>\n'
+                    'int main() { hipStream_t s = nullptr; return s ? 1 : 0; }\n')
+        r = subprocess.run([cxx, "-std=c++17", "-Wall", "-Werror", "-fsyntax-only",
+                            "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER), "-I",
+                            "/opt/rocm/include", cpp], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
 
 
 def dual(**kw):
