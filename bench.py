@@ -64,6 +64,12 @@ def parse():
                         "x query tokens) and print one JSON line with the table")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cold (flushed) timing passes (profiling runs)")
+    p.add_argument("--profile-commands", metavar="OUT_DIR",
+                   help="print the rocprofv3 commands whose output --summarize-profiles reads")
+    p.add_argument("--summarize-profiles", metavar="OUT_DIR",
+                   help="turn the rocprofv3 CSV output under OUT_DIR into the summaries in profiles/")
     return p.parse_args()
 
 
@@ -147,7 +153,8 @@ def decode_kernel_name(h_q):
     return "decode_w32_kernel" if h_q % 32 == 0 else "decode_tile16_kernel"
 
 
-def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_splits=0):
+def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_splits=0,
+                 no_cold=False):
     import torch
     t_gen = time.time()
     dual = W.dual_workload(name) is not None
@@ -262,7 +269,7 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
     # back while the decode runs; a second pass evicts with a 1 GiB read
     # (clean lines) instead.
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
-    n_cold = min(steps, COLD_LAUNCHES)
+    n_cold = 0 if no_cold else min(steps, COLD_LAUNCHES)
 
     def timed_after(evict):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -278,8 +285,8 @@ def bench_decode(lib, W, name, steps, warmup, nsets, time_graph, dev, force_spli
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs])
 
-    cold_ms = timed_after(lambda k, acc: flush.fill_(k + 1))
-    cold_read_ms = timed_after(lambda k, acc: acc.add_(flush.sum()))
+    cold_ms = timed_after(lambda k, acc: flush.fill_(k + 1)) if n_cold else np.array([np.nan])
+    cold_read_ms = timed_after(lambda k, acc: acc.add_(flush.sum())) if n_cold else np.array([np.nan])
     del flush
     acc = decode_accounting(sets, wl)
     dec_avg = float(dec_ms.mean())
@@ -439,9 +446,200 @@ def cpu_baseline(W, name, budget_s=12.0):
                 seconds=t_app + t_dec)
 
 
+# --------------------------------------------------------------------------- profiles
+# rocprofv3 runs behind the summaries in profiles/: a kernel trace per
+# workload, counter passes (each within one pass's per-block counter limits)
+# for the decode workloads, and a plain 1 GiB copy that calibrates the HBM
+# byte counters.
+PROFILE_TRACE = ["decode_h64", "decode_h128_varlen", "decode_h16_mtp", "decode_h16_mtp_dual",
+                 "decode_h64_ds_mla", "prefill_dual_h64_t4096", "append_write", "append_write_fp16",
+                 "append_write_fused"]
+PROFILE_COUNTERS = ["decode_h64", "decode_h128_varlen", "decode_h16_mtp"]
+COUNTER_PASSES = {
+    "util": "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
+    "insts": ("SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA SQ_INSTS_VALU "
+              "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD SQ_WAVES"),
+    "mem": "TA_TA_BUSY SQ_ACTIVE_INST_VMEM SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+SIMD_NUM = 1024                # MI355X: 256 CUs x 4 SIMDs
+CU_NUM = 256
+
+
+def profile_bench_args(w, trace):
+    if w.startswith("append"):
+        return f"--only {w} --steps 50 --warmup 5"
+    sets = "" if trace else " --sets 2"
+    steps = "--steps 100 --warmup 10" if trace else "--steps 6 --warmup 1"
+    if w.startswith("prefill"):
+        steps = "--steps 20 --warmup 2" if trace else "--steps 2 --warmup 1"
+    return f"--only {w} {steps}{sets} --no-cold"
+
+
+def profile_commands(out):
+    """(name, command) of every rocprofv3 run, each run from the repository
+    root with TMPDIR=/tmp."""
+    cmds = []
+    for w in PROFILE_TRACE:
+        cmds.append((f"kt_{w}", f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/kt_{w} "
+                                f"-o run -- python3 bench.py {profile_bench_args(w, True)}"))
+    for w in PROFILE_COUNTERS:
+        for tag, ctrs in COUNTER_PASSES.items():
+            cmds.append((f"pmc_{tag}_{w}", f"rocprofv3 --pmc {ctrs} --output-format csv -d "
+                                           f"{out}/pmc_{tag}_{w} -o run -- python3 bench.py "
+                                           f"{profile_bench_args(w, False)}"))
+    for tag in ("fetch", "write"):
+        cmds.append((f"pmc_{tag}_copy", f"rocprofv3 --pmc {COUNTER_PASSES[tag]} --output-format csv -d "
+                                        f"{out}/pmc_{tag}_copy -o run -- python3 bench.py --calibrate-copy"))
+    return cmds
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def _per_dispatch(d, library_only=True):
+    """{kernel: {counter: [value per dispatch]}} from a counter-collection CSV
+    (rows of one dispatch and counter summed over instances); the library's
+    kernels only, unless library_only is false (the copy calibration)."""
+    import collections
+    path = _find(d, "counter_collection.csv")
+    acc = collections.defaultdict(float)
+    for r in _csv_rows(path):
+        if library_only and "nvfp4::" not in r["Kernel_Name"]:
+            continue
+        acc[(_short(r["Kernel_Name"]), r["Counter_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (k, c, _), v in acc.items():
+        out[k][c].append(v)
+    return out
+
+
+def summarize_profiles(out):
+    """Writes profiles/<w>_kernel_trace.txt, profiles/<w>_counters.txt and
+    profiles/traffic_<w>.json from the runs of profile_commands(out)."""
+    cmds = dict(profile_commands(out))
+    pdir = os.path.join(ROOT, "profiles")
+    os.makedirs(pdir, exist_ok=True)
+    h = source_hash()
+    # kernel traces: per-dispatch durations
+    for w in PROFILE_TRACE:
+        path = _find(os.path.join(out, f"kt_{w}"), "kernel_trace.csv")
+        if path is None:
+            continue
+        durs = {}
+        for r in _csv_rows(path):
+            k = _short(r["Kernel_Name"])
+            if "nvfp4" not in k:
+                continue
+            durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines = [f"# rocprofv3 kernel trace, workload {w} (library source hash {h})",
+                 f"# command (repository root, TMPDIR=/tmp): {cmds['kt_' + w]}",
+                 "# every dispatch of the run: eager reference, graph checks, warmup and timed steps;",
+                 "# for the append workloads the pool fill is included (min/median are the steps)",
+                 f"{'kernel':58s} {'calls':>6s} {'median_us':>10s} {'mean_us':>9s} {'min_us':>8s} {'max_us':>8s}"]
+        for k, v in sorted(durs.items()):
+            a = np.array(v)
+            lines.append(f"{k:58s} {len(a):6d} {np.median(a):10.2f} {a.mean():9.2f} {a.min():8.2f} {a.max():8.2f}")
+        with open(os.path.join(pdir, f"{w}_kernel_trace.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    # HBM byte calibration: a plain copy of 1 GiB
+    try:
+        cf = _per_dispatch(os.path.join(out, "pmc_fetch_copy"), library_only=False)
+        cw = _per_dispatch(os.path.join(out, "pmc_write_copy"), library_only=False)
+        kf = max(cf, key=lambda k: np.mean(cf[k]["FETCH_SIZE"]))
+        kw = max(cw, key=lambda k: np.mean(cw[k]["WRITE_SIZE"]))
+        fetch_kib, write_kib = float(np.mean(cf[kf]["FETCH_SIZE"])), float(np.mean(cw[kw]["WRITE_SIZE"]))
+        fscale, wscale = (1 << 30) / (fetch_kib * 1024), (1 << 30) / (write_kib * 1024)
+    except (OSError, TypeError, ValueError):
+        fscale = wscale = None
+    for w in PROFILE_COUNTERS:
+        per = {}
+        for tag in COUNTER_PASSES:
+            d = os.path.join(out, f"pmc_{tag}_{w}")
+            if os.path.isdir(d):
+                for k, cs in _per_dispatch(d).items():
+                    for c, vals in cs.items():
+                        per.setdefault(k, {})[c] = float(np.mean(vals))
+        if not per:
+            continue
+        lines = [f"# rocprofv3 counters, workload {w} (library source hash {h}); mean per dispatch",
+                 "# commands (repository root, TMPDIR=/tmp):"]
+        lines += [f"#   {cmds[f'pmc_{t}_{w}']}" for t in COUNTER_PASSES]
+        lines += [f"#   {cmds['pmc_fetch_copy']}", f"#   {cmds['pmc_write_copy']}",
+                  "# derived: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 * 1024 SIMDs)",
+                  "#   (GRBM_GUI_ACTIVE is summed over the 8 XCDs); valu_busy = SQ_ACTIVE_INST_VALU /",
+                  "#   (GRBM_GUI_ACTIVE/8 * 256 CUs); mfma_tflop = SQ_INSTS_VALU_MFMA_MOPS_F16+BF16 * 512;",
+                  "#   HBM bytes = FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale (KiB, copy-calibrated)"]
+        traffic = {}
+        for k, c in sorted(per.items()):
+            lines.append(f"[{k}]")
+            for name in sorted(c):
+                lines.append(f"  {name:32s} {c[name]:18.1f}")
+            gui = c.get("GRBM_GUI_ACTIVE")
+            if gui:
+                cyc = gui / 8
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                    lines.append(f"  {'mfma_busy':32s} {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * SIMD_NUM):18.3f}")
+                if "SQ_ACTIVE_INST_VALU" in c:
+                    lines.append(f"  {'valu_busy':32s} {c['SQ_ACTIVE_INST_VALU'] / (cyc * CU_NUM):18.3f}")
+                if "SQ_LDS_IDX_ACTIVE" in c:
+                    lines.append(f"  {'lds_active':32s} {c['SQ_LDS_IDX_ACTIVE'] / (cyc * CU_NUM):18.3f}")
+                lines.append(f"  {'gpu_busy_cycles_per_xcd':32s} {cyc:18.1f}")
+            mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+            if mops:
+                lines.append(f"  {'mfma_gflop':32s} {mops * 512 / 1e9:18.3f}")
+            if fscale and "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+                rb, wb = c["FETCH_SIZE"] * 1024 * fscale, c["WRITE_SIZE"] * 1024 * wscale
+                lines.append(f"  {'hbm_read_mb':32s} {rb / 1e6:18.3f}")
+                lines.append(f"  {'hbm_write_mb':32s} {wb / 1e6:18.3f}")
+                traffic[k] = {"read_bytes": rb, "write_bytes": wb, "fetch_kib_raw": c["FETCH_SIZE"],
+                              "write_kib_raw": c["WRITE_SIZE"]}
+        if fscale:
+            lines.append(f"# calibration: the 1 GiB copy reads FETCH_SIZE {fetch_kib:.0f} KiB and WRITE_SIZE "
+                         f"{write_kib:.0f} KiB per dispatch: fetch_scale {fscale:.4f}, write_scale {wscale:.4f}")
+        with open(os.path.join(pdir, f"{w}_counters.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        # the decode call's kernels: the decode and, with splits, the combine
+        dec = {k: v for k, v in traffic.items() if "decode" in k or "combine" in k}
+        if dec:
+            doc = {"workload": w, "source_hash": h,
+                   "bytes_per_launch": sum(v["read_bytes"] + v["write_bytes"] for v in dec.values()),
+                   "kernels": dec, "fetch_scale": fscale, "write_scale": wscale,
+                   "calibration": f"plain 1 GiB device copy: FETCH_SIZE {fetch_kib:.0f} KiB, "
+                                  f"WRITE_SIZE {write_kib:.0f} KiB per dispatch",
+                   "commands": [cmds[f"pmc_fetch_{w}"], cmds[f"pmc_write_{w}"], cmds["pmc_fetch_copy"],
+                                cmds["pmc_write_copy"]]}
+            with open(os.path.join(pdir, f"traffic_{w}.json"), "w") as f:
+                json.dump(doc, f, indent=1)
+    print(f"profiles written for source hash {h}")
+
+
 # --------------------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.profile_commands:
+        for _, c in profile_commands(args.profile_commands):
+            print(c)
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested): the decode would shard by rows, by heads, or by context with the combine "
@@ -485,7 +683,7 @@ def main():
             # a prefill's query rows already span its pool: one index set
             nsets = 1 if args.only.startswith("prefill") else args.sets
             res = bench_decode(lib, W, args.only, args.steps, args.warmup, nsets, use_graph, dev,
-                               args.splits)
+                               args.splits, no_cold=args.no_cold)
         print(json.dumps(res))
         return
 
