@@ -27,36 +27,25 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_mag(float q) {
   return (b >> 20) - (120u << 3);            // rebias exponent 127 -> 7
 }
 
-// Magnitude code (0..7) of |x| on the E2M1 grid {0,.5,1,1.5,2,3,4,6} * s,
-// ties to the even code.  The thresholds t_k = s*{.25,.75,1.25,1.75,2.5,3.5,5}
-// between codes k and k+1 are exact fp32 products; a tie at t_k goes to the
-// even one of k and k+1, hence >= for odd k and > for even k.  The code is
-// found bit by bit: bit 2 from t_3, bit 1 from t_1 or t_5, bit 0 from
-// t_0, t_2, t_4 or t_6.  A zero scale gives infinite thresholds (code 0).
-struct E2m1Thresholds {
-  float t[7];
-  __device__ __forceinline__ explicit E2m1Thresholds(float s) {
-    const float inf = __builtin_inff();
-    t[0] = s == 0.0f ? inf : 0.25f * s;
-    t[1] = s == 0.0f ? inf : 0.75f * s;
-    t[2] = s == 0.0f ? inf : 1.25f * s;
-    t[3] = s == 0.0f ? inf : 1.75f * s;
-    t[4] = s == 0.0f ? inf : 2.5f * s;
-    t[5] = s == 0.0f ? inf : 3.5f * s;
-    t[6] = s == 0.0f ? inf : 5.0f * s;
-  }
-  // the selects are written as bit masks so that they stay selects
-  __device__ __forceinline__ static float pick(uint32_t m, float x, float y) {   // m ? x : y
-    return __uint_as_float((__float_as_uint(x) & m) | (__float_as_uint(y) & ~m));
-  }
-  __device__ __forceinline__ uint32_t code(float a) const {
-    const uint32_t m2 = 0u - (uint32_t)(a >= t[3]);
-    const uint32_t m1 = 0u - (uint32_t)(a >= pick(m2, t[5], t[1]));
-    const float tl = pick(m2, pick(m1, t[6], t[4]), pick(m1, t[2], t[0]));
-    const uint32_t b0 = (uint32_t)(a > tl);
-    return (m2 & 4u) | (m1 & 2u) | b0;
-  }
-};
+// The E2M1 code of x / s, rounded to nearest with ties to the even code,
+// comes from the hardware fp32 -> E2M1 convert (round to nearest even,
+// saturating at 6, sign kept, including for zero) applied to a quotient that
+// rounds the same way as the exact x / s:
+//   * q = |x| * r with r within one unit in the last place of 1/s is within
+//     2^-21 of |x| / s for every quotient below 8;
+//   * a tie t (a midpoint of the grid, .25 .. 5) has |x| = t s exactly, and
+//     otherwise |x| and t s are different bf16 values (t s has at most 7
+//     significant bits), at least 2^-8 t >= 2^-10 apart relative to s;
+//   * so rounding q to a multiple of 2^-12 returns an exact tie exactly and
+//     leaves every other quotient on its side of every tie.
+// Quotients from 8 up all give code 7, so q is clamped to 8 first; a zero
+// scale gives q = 0 (code 0, sign kept).
+__device__ __forceinline__ float e2m1_quotient(float x, float r) {
+#pragma clang fp contract(off)
+  float q = fminf(fabsf(x) * r, 8.0f);
+  q = (q + 3072.0f) - 3072.0f;          // 3072 = 1.5 * 2^11: its ulp is 2^-12
+  return __builtin_copysignf(q, x);
+}
 
 // A 16-bit input element (bf16, or fp16 when kF16) widened to fp32, exactly.
 template <bool kF16>
@@ -189,13 +178,18 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
     for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     const uint32_t scode = e4m3_rne_sat_mag(__fdiv_rn(amax, 6.0f));
-    const E2m1Thresholds th(e4m3x2_to_f32<0>(scode).x);
+    const float sv = e4m3x2_to_f32<0>(scode).x;
+    const float rs = sv == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sv);
+    // codes 2i (low nibble) and 2i+1 of byte i
     uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      uint32_t code = th.code(fabsf(x[i])) | ((__float_as_uint(x[i]) >> 28) & 8u);
-      packed |= code << (4 * i);
-    }
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, e2m1_quotient(x[0], rs),
+                                                      e2m1_quotient(x[1], rs), 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, e2m1_quotient(x[2], rs),
+                                                      e2m1_quotient(x[3], rs), 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, e2m1_quotient(x[4], rs),
+                                                      e2m1_quotient(x[5], rs), 1.0f, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, e2m1_quotient(x[6], rs),
+                                                      e2m1_quotient(x[7], rs), 1.0f, 3);
     // the previous token's record has been read out of the staging area
     __builtin_amdgcn_wave_barrier();
     reinterpret_cast<uint32_t*>(r)[lane] = packed;
