@@ -111,7 +111,7 @@ __device__ __forceinline__ float rope_turn(float xl, int64_t pos, const NormRope
 // each record is assembled in LDS and written with 16-byte stores (22 or 27).
 // The input is bf16, or fp16 when kF16 (352-byte record only): every fp16 or
 // bf16 value is exact in fp32, so the rounding below is the same for both.
-constexpr int kTokW = 4;
+constexpr int kTokW = 2;
 
 // With kFused the tokens first go through the norm + rotary prologue and
 // are rounded to bf16 (bf16 inputs only); a token whose position lies outside
