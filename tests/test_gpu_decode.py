@@ -143,6 +143,28 @@ def test_combine_matches_oracle(lib):
         assert_decode_close(o, lse, o_ref, l_ref, "combine")
 
 
+def test_combine_turns_a_nan_partial_lse_into_a_nan_row(lib):
+    # a decode workgroup whose bounded wait ran out marks its partial with a
+    # NaN LSE; the merge must not hide it behind the other splits' maxima
+    rng = np.random.default_rng(5)
+    p, r, h = 6, 5, 16
+    o_part = rng.standard_normal((p, r, h, 512)).astype(np.float32)
+    lse_part = (rng.standard_normal((p, r, h)) * 3).astype(np.float32)
+    marked = [(0, 1, 3), (5, 4, 0), (2, 2, 15)]      # (split, row, head); split 5 is in the tail group
+    for s, i, j in marked:
+        lse_part[s, i, j] = np.nan
+    lse_part[:, 3, 7] = -np.inf
+    lse_part[4, 3, 7] = np.nan                      # NaN among empty partials
+    o_part[np.isneginf(lse_part)] = 0
+    o, lse = lib.combine(torch.from_numpy(o_part).to(DEV), torch.from_numpy(lse_part).to(DEV),
+                         sink=torch.from_numpy(rng.standard_normal(h).astype(np.float32)).to(DEV))
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    bad = np.isnan(lse_part).any(axis=0)
+    assert np.isnan(lse[bad]).all() and np.isnan(o[bad]).all()
+    assert np.isfinite(o[~bad]).all() and not np.isnan(lse[~bad]).any()
+
+
 def full_workload(lib, wl):
     """GPU pool filled by the HIP quantize-append from the workload latents;
     expected values from the oracle quantizing the same latents.  Every row
