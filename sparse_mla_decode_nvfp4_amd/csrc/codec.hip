@@ -38,11 +38,13 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_mag(float q) {
 //     significant bits), at least 2^-8 t >= 2^-10 apart relative to s;
 //   * so rounding q to a multiple of 2^-12 returns an exact tie exactly and
 //     leaves every other quotient on its side of every tie.
-// Quotients from 8 up all give code 7, so q is clamped to 8 first; a zero
-// scale gives q = 0 (code 0, sign kept).
+// Quotients above 5 all give code 7 (the convert saturates) and stay finite
+// for finite inputs (q <= amax / s, and s is amax / 6 rounded unless it
+// saturates at 448), so they need no clamp: adding and removing 3072 leaves
+// them above 5.  A zero scale gives q = 0 (code 0, sign kept).
 __device__ __forceinline__ float e2m1_quotient(float x, float r) {
 #pragma clang fp contract(off)
-  float q = fminf(fabsf(x) * r, 8.0f);
+  float q = fabsf(x) * r;
   q = (q + 3072.0f) - 3072.0f;          // 3072 = 1.5 * 2^11: its ulp is 2^-12
   return __builtin_copysignf(q, x);
 }
