@@ -58,6 +58,7 @@ def run_small(lib, recs, q, idx, sink, nblocks, bs, splits, scale=1.0 / 24):
     (1, 1, 16, 64, 1), (2, 1, 16, 1, 1), (3, 2, 16, 17, 1), (2, 2, 32, 100, 1),
     (1, 1, 64, 333, 1), (1, 2, 128, 200, 1), (2, 1, 16, 1000, 3), (1, 1, 64, 512, 0),
     (2, 1, 128, 700, 4), (1, 1, 16, 2048, 0), (1, 1, 16, 31, 2), (1, 1, 48, 129, 5),
+    (3, 1, 96, 150, 2), (1, 3, 160, 90, 1),
 ])
 def test_small_cases(lib, b, s_q, h, topk, splits):
     note(f"small case b={b} s_q={s_q} h={h} topk={topk} splits={splits}")
