@@ -364,6 +364,15 @@ def bench_append(lib, W, steps, warmup, dev, fp16=False, fused=False):
         ev[k][1].record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the same launches back to back between one event pair: the kernel's
+    # throughput when appends queue up (no host gap between launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    b2b_ms = e0.elapsed_time(e1) / steps
     mapped = int((wl.slot_mapping >= 0).sum())
     # compulsory: each mapped token's inputs and record, every slot id (and,
     # fused, its position; the weight and the table rows are cache-resident)
@@ -372,7 +381,11 @@ def bench_append(lib, W, steps, warmup, dev, fp16=False, fused=False):
                bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9,
                tokens_per_s=mapped / (ms * 1e-3))
     res["hbm_frac"] = res["gbps"] / PEAK_HBM_GBS
-    log(f"{name}: {ms * 1e3:.1f} us, {res['gbps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM)")
+    res["b2b_ms"] = b2b_ms
+    res["b2b_gbps"] = nbytes / (b2b_ms * 1e-3) / 1e9
+    res["b2b_hbm_frac"] = res["b2b_gbps"] / PEAK_HBM_GBS
+    log(f"{name}: {ms * 1e3:.1f} us per launch ({res['gbps']:.0f} GB/s, {100 * res['hbm_frac']:.1f}% HBM); "
+        f"back to back {b2b_ms * 1e3:.1f} us ({res['b2b_gbps']:.0f} GB/s, {100 * res['b2b_hbm_frac']:.1f}% HBM)")
     del cache
     torch.cuda.empty_cache()
     return res

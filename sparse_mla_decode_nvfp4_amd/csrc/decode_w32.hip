@@ -85,7 +85,9 @@ struct LdsW32 {
   static constexpr int kOffFlag = kOffStat + kWaves * 2 * 32 * 4 + 2 * 32 * 4;
   // published and consumed counters per wave, then the lost-wait flag
   static constexpr int kOffFail = kOffFlag + 2 * kWaves * 4;
-  static constexpr int kBytes = kOffFail + 16;
+  // the sink logits of the group's 32 heads
+  static constexpr int kOffSink = kOffFail + 16;
+  static constexpr int kBytes = kOffSink + 32 * 4;
   // merge: 4 slots of 4 KB per wave in round one, then an 8 KB output
   // stage per wave (past the round-two slots for four pairs, from 0 for two)
   static constexpr int kOffStage = kPairs == 4 ? 16 * 4096 : 0;
@@ -221,6 +223,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   lds_u32* const flag = (lds_u32*)(lds + L::kOffFlag);   // [wave]: chunks whose partial S is published
   lds_u32* const consumed = flag + kWavesP;              // [wave]: partner chunks read (one buffer)
   lds_u32* const failed = (lds_u32*)(lds + L::kOffFail); // a wave gave up waiting for its partner
+  lds_f32* const sinkl = (lds_f32*)(lds + L::kOffSink);  // [32] sink logits (without splits)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -321,6 +324,10 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
       for (int j = 0; j < 8; j++)
         raw[j] = *reinterpret_cast<const u32x4*>(qrow + 16 * (16 * hf + 4 * g + (j >> 1)) + 8 * (j & 1));
       raw[8] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 32 * hf + 8 * g);
+      // wave 0 also fetches the group's sink logits for the epilogue; they
+      // arrive with its Q elements, which it waits for next
+      float sink_v = 0.f;
+      if (wave == 0 && a.splits == 1 && a.sink != nullptr) sink_v = a.sink[h0 + (lane & 31)];
       uint32_t amax_bits = 0;
 #pragma unroll
       for (int j = 0; j < 9; j++)
@@ -332,6 +339,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
       amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 16));
       amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 32));
       if (g == 0) qmax[hf * 32 + 16 * pr + n] = amax_bits;
+      if (wave == 0 && lane < 32) sinkl[lane] = sink_v;
     }
     if (lane == 0) {
       flag[wave] = 0;
@@ -660,6 +668,11 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   }
 
   // ---- merge the four pairs (same heads and output dims, disjoint tokens)
+  // Lane l keeps the merged statistics of head hh = l % 32 of the group: the
+  // maximum M over the pairs' running maxima, the denominator L, and this
+  // pair's weight exp2(m_pair - M); accumulator rows fetch them by lane.
+  const bool single = a.splits == 1;
+  const int hh = lane & 31;
   if (lost && lane == 0) __hip_atomic_store(failed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   sum_blocks(l_part[0], l_part[1]);
   if (g == 0) {
@@ -671,29 +684,33 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   }
   lds_sync_p();
   const bool wg_failed = *failed != 0u;
-  float Mh[2], Lh[2], fown[2];
-#pragma unroll
-  for (int b = 0; b < 2; b++) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < kPairs; p++) M = fmaxf(M, stat[((2 * p + hf) * 2) * 32 + 16 * b + n]);
-    float L = 0.f;
+  float Mh, Lh, fown;
+  {
+    // every pair's statistics are read up front (reads under a branch would
+    // wait for each one in turn); an empty pair (m = -inf) adds exactly zero
+    float mp[kPairs], lp[kPairs];
 #pragma unroll
     for (int p = 0; p < kPairs; p++) {
-      const float mp = stat[((2 * p + hf) * 2) * 32 + 16 * b + n];
-      if (mp != -INFINITY) L += stat[((2 * p + hf) * 2 + 1) * 32 + 16 * b + n] * __builtin_amdgcn_exp2f(mp - M);
+      mp[p] = stat[((2 * p + hf) * 2) * 32 + hh];
+      lp[p] = stat[((2 * p + hf) * 2 + 1) * 32 + hh];
     }
-    Mh[b] = M;
-    Lh[b] = L;
-    fown[b] = (m_use[b] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_use[b] - M);
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kPairs; p++) M = fmaxf(M, mp[p]);
+    float L = 0.f;
+#pragma unroll
+    for (int p = 0; p < kPairs; p++)
+      L += mp[p] != -INFINITY ? lp[p] * __builtin_amdgcn_exp2f(mp[p] - M) : 0.f;
+    Mh = M;
+    Lh = L;
+    // this wave's own running max of head hh is the value it posted
+    const float mown = mp[pr];
+    fown = (mown == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mown - M);
   }
-  // this pair's weight exp2(m_pair - M) on each accumulator row
+  // this pair's weight on each accumulator row
   float fr[16];
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int hr = acc_row(r, kg);
-    fr[r] = __shfl(hr < 16 ? fown[0] : fown[1], hr & 15);
-  }
+  for (int r = 0; r < 16; r++) fr[r] = __shfl(fown, acc_row(r, kg));
   // Two rounds of pairwise sums through LDS (slots of 16 floats x 64 lanes,
   // lane-contiguous, over the first 128 KB): round 1 pairs p and p^1 (even p
   // keeps blocks 0..3, odd p 4..7), round 2 pairs p and p^2 (each keeps two
@@ -768,23 +785,14 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   }
 
   // ---- normalise and write this wave's two output blocks
-  const bool single = a.splits == 1;
   float inv[16];
   {
-    float invh[2];
+    float denom = Lh;
+    if (single && a.sink != nullptr && Lh > 0.f) denom += __builtin_amdgcn_exp2f(sinkl[hh] * kLog2eP - Mh);
+    float invh = Lh > 0.f ? 1.0f / denom : 0.f;
+    if (wg_failed) invh = __builtin_nanf("");
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
-      float denom = Lh[b];
-      if (single && a.sink != nullptr && Lh[b] > 0.f)
-        denom += __builtin_amdgcn_exp2f(a.sink[h0 + 16 * b + n] * kLog2eP - Mh[b]);
-      invh[b] = Lh[b] > 0.f ? 1.0f / denom : 0.f;
-      if (wg_failed) invh[b] = __builtin_nanf("");
-    }
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int hr = acc_row(r, kg);
-      inv[r] = __shfl(hr < 16 ? invh[0] : invh[1], hr & 15);
-    }
+    for (int r = 0; r < 16; r++) inv[r] = __shfl(invh, acc_row(r, kg));
   }
   const size_t orow = (size_t)row * a.h_q + h0;
   const size_t prow = ((size_t)split * a.rows + row) * a.h_q + h0;
@@ -851,14 +859,11 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     stage_blocks(IntC<6>{});
     store_blocks(6);
   }
-  if (wave == 0 && g == 0) {
-#pragma unroll
-    for (int b = 0; b < 2; b++) {
-      float lse = Lh[b] > 0.f ? (Mh[b] + __log2f(Lh[b])) * kLn2P : -INFINITY;
-      if (wg_failed) lse = __builtin_nanf("");
-      if (single) a.lse[orow + 16 * b + n] = lse;
-      else a.lse_part[prow + 16 * b + n] = lse;
-    }
+  if (wave == 0 && lane < 32) {
+    float lse = Lh > 0.f ? (Mh + __log2f(Lh)) * kLn2P : -INFINITY;
+    if (wg_failed) lse = __builtin_nanf("");
+    if (single) a.lse[orow + hh] = lse;
+    else a.lse_part[prow + hh] = lse;
   }
 }
 
