@@ -346,10 +346,9 @@ decode_tile16_kernel(DecodeArgs a) {
   f32x4 acc_o[8];
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) acc_o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max (log2 units) of head n (for P) and of heads 4g+r (O rows);
-  // every wave derives them from the same LDS values, so they agree
+  // running max (log2 units) of head n; every wave derives it from the same
+  // LDS values, so they agree, and lane 4g+r holds that of O row 4g+r
   float m_n = -INFINITY;
-  float m_r[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float l_part = 0.f;          // this lane's share of head n's denominator
 
   // V tile addresses.  Write (k-step 2c+h): chunk 2 blk(g, c) + h = 16g + 2c
@@ -424,29 +423,23 @@ decode_tile16_kernel(DecodeArgs a) {
     if (g == 0) tmax[wave][n] = bm;
     lds_barrier();                        // every wave's maxima posted
 
-    // ---- running max update (same rule in every wave), lazy O rescale
+    // ---- running max update (same rule in every wave), lazy O rescale.
+    // The O rows' factors come from the lanes of their heads, only when some
+    // head's max was raised.
     float tm_n = tmax[0][n];
 #pragma unroll
     for (int w = 1; w < kWaves; w++) tm_n = fmaxf(tm_n, tmax[w][n]);
-    if (tm_n > m_n + kLazyThreshold) {
-      l_part *= fast_exp2(m_n - tm_n);    // m_n = -inf gives 0 (l_part is 0 then)
+    const bool raise = tm_n > m_n + kLazyThreshold;
+    float alpha_n = 1.0f;
+    if (raise) {
+      alpha_n = fast_exp2(m_n - tm_n);    // m_n = -inf gives 0 (l_part and O are 0 then)
+      l_part *= alpha_n;
       m_n = tm_n;
     }
-    bool any_rescale = false;
-    float alpha[4];
+    if (__any(raise)) {
+      float alpha[4];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      float tm = tmax[0][4 * g + r];
-#pragma unroll
-      for (int w = 1; w < kWaves; w++) tm = fmaxf(tm, tmax[w][4 * g + r]);
-      alpha[r] = 1.0f;
-      if (tm > m_r[r] + kLazyThreshold) {
-        alpha[r] = fast_exp2(m_r[r] - tm);
-        m_r[r] = tm;
-        any_rescale = true;
-      }
-    }
-    if (__any(any_rescale)) {
+      for (int r = 0; r < 4; r++) alpha[r] = __shfl(alpha_n, 4 * g + r);
 #pragma unroll
       for (int nb = 0; nb < 8; nb++)
 #pragma unroll
