@@ -364,15 +364,22 @@ def bench_append(lib, W, steps, warmup, dev, fp16=False, fused=False):
         ev[k][1].record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    # the same launches back to back between one event pair: the kernel's
-    # throughput when appends queue up (no host gap between launches)
+    # the same launches back to back, replayed from one HIP graph between one
+    # event pair: the kernel's throughput when appends queue up, without the
+    # host's per-call time between launches
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            run()
+    graph.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
-        run()
+    graph.replay()
     e1.record()
     torch.cuda.synchronize()
     b2b_ms = e0.elapsed_time(e1) / steps
+    del graph
     mapped = int((wl.slot_mapping >= 0).sum())
     # compulsory: each mapped token's inputs and record, every slot id (and,
     # fused, its position; the weight and the table rows are cache-resident)
