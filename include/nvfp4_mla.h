@@ -305,7 +305,9 @@ size_t nvfp4_mla_sparse_decode_workspace_size(int32_t batch, int32_t s_q,
  *   num_splits 0 = planner's choice, else 1..NVFP4_MLA_MAX_SPLITS
  * h_q must be a multiple of 16 (1..16 * 16), topk in [1, 65536].
  * The decode is one kernel launch, plus one combine launch when more than
- * one split runs.
+ * one split runs.  A call whose launches would exceed 2^32 - 1 work-items
+ * (rows * h_q * splits * 16 for the decode, rows * h_q * 64 for the combine)
+ * returns NVFP4_MLA_ERR_INVALID_ARGUMENT before any launch: split the batch.
  * Accuracy: K and V are exact; Q is exact for every element within 2^31 of
  * its head's largest magnitude; scores and sums are fp32; P enters PV as
  * fp16 hi + lo parts (about 2^-22 relative); O is rounded once to bf16 (with
@@ -435,6 +437,8 @@ int nvfp4_mla_sparse_decode_dual_ds_mla(const void* q_bf16, const uint8_t* kv_ca
  *   o_partial   [num_splits, rows, h_q, 512] float32 contiguous
  *   lse_partial [num_splits, rows, h_q] float32 contiguous
  *   out_bf16    [rows, h_q, 512] bf16;  lse [rows, h_q] float32
+ * num_splits in [1, 4096]; rows * h_q below 2^26 (one launch of 64
+ * work-items per row and head), else NVFP4_MLA_ERR_INVALID_ARGUMENT.
  */
 int nvfp4_mla_combine(const float* o_partial, const float* lse_partial,
                       int32_t num_splits, int64_t rows, int32_t h_q,

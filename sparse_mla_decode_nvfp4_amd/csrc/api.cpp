@@ -155,6 +155,23 @@ int plan_splits(int32_t rows, int32_t h_q, int32_t topk, int cus) {
   return (int)want;
 }
 
+// A decode launch's work-items must fit HIP's 32-bit grid size: the decode
+// kernel runs rows * (h_q / 32 or / 16) * splits workgroups of at most 512
+// work-items (256 for the 16-head kernel), and with splits the combine runs
+// 64 work-items per (row, head).  Larger calls are rejected, never truncated.
+int check_launch_size(int64_t rows, int32_t h_q, int32_t splits) {
+  const bool w32 = nvfp4::decode_uses_w32(h_q);
+  const int64_t wgs = rows * (w32 ? h_q / 32 : h_q / 16) * (int64_t)splits;
+  const int64_t items = wgs * (w32 ? 512 : 256);
+  const int64_t combine_items = splits > 1 ? rows * h_q * 64 : 0;
+  if (items > INT64_C(0xFFFFFFFF) || combine_items > INT64_C(0xFFFFFFFF))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                "a decode of %lld rows x %d heads with %d splits needs %lld decode work-items "
+                "(and %lld for the combine); one launch holds at most 2^32 - 1: split the batch",
+                (long long)rows, h_q, splits, (long long)items, (long long)combine_items);
+  return NVFP4_MLA_OK;
+}
+
 // Workspace layout for splits > 1 (each region 256-byte aligned):
 //   o_part   [splits, rows, h_q, 512] fp32 (the 32-head kernel fills the first half
 //            of it with fp16 partials)
@@ -334,6 +351,9 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   if (!std::isfinite(softmax_scale))
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   const int64_t rows = (int64_t)batch * s_q;
+  // the planner never picks fewer than one split
+  rc = check_launch_size(rows, h_q, num_splits > 0 ? num_splits : 1);
+  if (rc) return rc;
   if (rows > 0) {
     if (!q_bf16 || !out_bf16 || !lse)
       return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "q, indices, out and lse must be non-NULL");
@@ -351,6 +371,8 @@ int sparse_decode_impl(const char* fn, const void* q_bf16, const uint8_t* kv_cac
   rc = check_device(&cus);
   if (rc) return rc;
   int splits = num_splits == 0 ? plan_splits((int32_t)rows, h_q, topk, cus) : num_splits;
+  rc = check_launch_size(rows, h_q, splits);
+  if (rc) return rc;
   const size_t need = workspace_bytes(rows, h_q, splits);
   if (static_scratch && need > 0) {
     if (need > kScratchBytes)
@@ -683,8 +705,11 @@ int nvfp4_mla_combine(const float* o_partial, const float* lse_partial, int32_t 
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "num_splits = %d must be in [1, 4096]", num_splits);
   if (rows < 0 || h_q < 1)
     return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "rows must be >= 0 and h_q >= 1");
-  if (rows * (int64_t)h_q > INT64_C(0x7FFFFFFF))
-    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "rows * h_q too large");
+  // 64 work-items per (row, head) in one launch of at most 2^32 - 1
+  if (rows * (int64_t)h_q * 64 > INT64_C(0xFFFFFFFF))
+    return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT,
+                "rows * h_q = %lld too large: one launch holds at most 2^26 - 1 (row, head) "
+                "pairs (64 work-items each)", (long long)(rows * (int64_t)h_q));
   if (rows > 0) {
     if (!o_partial || !lse_partial || !out_bf16 || !lse)
       return fail(NVFP4_MLA_ERR_INVALID_ARGUMENT, "o_partial, lse_partial, out, lse must be non-NULL");

@@ -131,6 +131,12 @@ def dec(**kw):
     (dict(q=ctypes.c_void_p(0x100008)), "aligned"),
     (dict(out=ctypes.c_void_p(0x100004)), "aligned"),
     (dict(sink=ctypes.c_void_p(0x100002)), "aligned"),
+    # one launch's work-items must fit HIP's 32-bit grid size: the 32-head
+    # kernel (8 groups x 2^21 rows x 512), the 16-head kernel (15 groups x
+    # 2^20 rows x 64 splits x 256) and the combine alone (96 x 2^20 x 64)
+    (dict(batch=2 ** 21, h_q=256), "work-items"),
+    (dict(batch=2 ** 20, h_q=240, splits=64), "work-items"),
+    (dict(batch=2 ** 20, h_q=96, splits=2), "work-items"),
 ])
 def test_sparse_decode_rejects_bad_arguments(kw, needle):
     assert dec(**kw) == m.ERR_INVALID_ARGUMENT
@@ -290,6 +296,9 @@ def test_combine_and_gather_reject_bad_arguments():
     assert lib.nvfp4_mla_combine(P16, P16, 0, 4, 16, NULL, P16, P16, NULL) == m.ERR_INVALID_ARGUMENT
     assert lib.nvfp4_mla_combine(P16, P16, 2, -1, 16, NULL, P16, P16, NULL) == m.ERR_INVALID_ARGUMENT
     assert lib.nvfp4_mla_combine(NULL, P16, 2, 4, 16, NULL, P16, P16, NULL) == m.ERR_INVALID_ARGUMENT
+    # 2^20 rows x 64 heads x 64 work-items exceeds one launch
+    assert lib.nvfp4_mla_combine(P16, P16, 2, 2 ** 20, 64, NULL, P16, P16, NULL) == m.ERR_INVALID_ARGUMENT
+    assert "too large" in m.last_error()
     assert lib.nvfp4_mla_dequantize_gather(P16, 4, 64, 64 * 352, P16, -1, P16, NULL) == m.ERR_INVALID_ARGUMENT
     assert lib.nvfp4_mla_dequantize_gather(P16, 4, 64, 64 * 352, NULL, 3, P16, NULL) == m.ERR_INVALID_ARGUMENT
     assert lib.nvfp4_mla_dequantize_gather(P16, 4, 64, 64 * 352, P16, 3,
