@@ -411,3 +411,32 @@ def test_binding_checks_dual_combine_append_and_gather_tensors():
     with pytest.raises(ValueError, match="out must be"):
         m.dequantize_gather(cache, torch.zeros(4, dtype=torch.int32),
                             out=torch.zeros((4, 512), dtype=torch.bfloat16))
+
+
+def test_the_package_never_imports_the_oracle():
+    # the product path (package import, library load, argument checks) runs
+    # with no oracle module loaded, and no package source names one
+    import subprocess
+    import sys
+    code = ("import sys, sparse_mla_decode_nvfp4_amd as m; m.lib(); m.check_format(); "
+            "import sparse_mla_decode_nvfp4_amd.workloads; "
+            "bad = [k for k in sys.modules if k == 'oracle' or k.startswith('oracle.')]; "
+            "assert not bad, bad")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    pkg = os.path.join(ROOT, "sparse_mla_decode_nvfp4_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            text = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), name
+
+
+def test_a_missing_library_fails_loudly():
+    # no fallback: with the shared library absent every call raises
+    import subprocess
+    import sys
+    code = ("import sparse_mla_decode_nvfp4_amd as m; m.LIB_PATH = '/nonexistent/libnvfp4_mla.so'\n"
+            "try:\n    m.abi_version()\nexcept m.NativeLibraryMissing as e:\n    print('raised', e)\n"
+            "else:\n    raise SystemExit('no error')")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
