@@ -259,12 +259,28 @@ decode_tile16_kernel(DecodeArgs a) {
     return resolve_rec<kDual>(a, v, p < t_end, p, src.topk0);
   };
 
-  // ---- prologue: indices of tiles 0 and 1, token bytes of tile 0 (before
-  // the Q set-up, which hides part of their latency)
+  // ---- prologue: indices of tiles 0 and 1, then this wave's Q elements
+  // (their latency overlaps the indices'), then the token bytes of tile 0
+  // once its indices are back; the Q set-up below overlaps their flight
   int tile = tile0;
-  const RecRef r0 = resolve(load_idx(tile), tile);
-  bool ok_cur = r0.ok;             // this lane's token of the current tile takes part
+  const int32_t idx0 = load_idx(tile);
   int32_t idx_nxt = load_idx(tile + 1);
+  constexpr int kQPer = (18 + kWaves - 1) / kWaves;   // k-steps per wave, at most
+  const uint16_t* qrow = a.q + ((size_t)row * a.h_q + h0 + n) * kQkDim;
+  u32x4 raw[kQPer];
+  // one unconditional load per k-step slot, its address picked without a
+  // branch (a load under a branch makes the compiler wait for all earlier
+  // loads, the record gathers included, before the next one); a wave with
+  // fewer than kQPer k-steps loads an in-row element it does not use
+#pragma unroll
+  for (int i = 0; i < kQPer; i++) {
+    const int ks = wave + kWaves * i;                 // uniform over the wave
+    const int off = ks < 16 ? 16 * blk(g, ks >> 1) + 8 * (ks & 1)
+                            : kNopeDim + 16 * g + 8 * min(ks - 16, 1);
+    raw[i] = *reinterpret_cast<const u32x4*>(qrow + off);
+  }
+  const RecRef r0 = resolve(idx0, tile);
+  bool ok_cur = r0.ok;             // this lane's token of the current tile takes part
   RawTok<F> cur;
   load_tok(cur, r0.ptr, g);
 
@@ -277,17 +293,6 @@ decode_tile16_kernel(DecodeArgs a) {
   h16x8 qB[18];
   float qscale;          // |softmax_scale| * log2(e) * 2^p of head n
   {
-    constexpr int kQPer = (18 + kWaves - 1) / kWaves;   // k-steps per wave, at most
-    const uint16_t* qrow = a.q + ((size_t)row * a.h_q + h0 + n) * kQkDim;
-    u32x4 raw[kQPer];
-#pragma unroll
-    for (int i = 0; i < kQPer; i++) {
-      const int ks = wave + kWaves * i;                 // uniform over the wave
-      if (ks < 16)
-        raw[i] = *reinterpret_cast<const u32x4*>(qrow + 16 * blk(g, ks >> 1) + 8 * (ks & 1));
-      else if (ks < 18)
-        raw[i] = *reinterpret_cast<const u32x4*>(qrow + kNopeDim + 16 * g + 8 * (ks - 16));
-    }
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < kQPer; i++)
