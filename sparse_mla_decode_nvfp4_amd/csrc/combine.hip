@@ -73,21 +73,22 @@ combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
   for (int s0 = 0; s0 < splits; s0 += 4) {
     float ls[4];
     float v[4][8];
+    // the four loads go out unconditionally (a load under a branch would
+    // wait for the one before it): past the last split they re-read it and
+    // its weight is zero
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const int s = s0 + u;
-      if (s < splits) {                        // uniform over the wave
-        ls[u] = lse_part[s * rh_total + rh];
-        load8(o_part + (s * rh_total + rh) * kVDim + dv0, v[u]);
-      } else {
-        ls[u] = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 8; i++) v[u][i] = 0.f;
-      }
+      const int s = min(s0 + u, splits - 1);
+      ls[u] = lse_part[s * rh_total + rh];
+      load8(o_part + (s * rh_total + rh) * kVDim + dv0, v[u]);
     }
+#pragma unroll
+    for (int u = 0; u < 4; u++) ls[u] = s0 + u < splits ? ls[u] : -INFINITY;
     nan_seen |= (ls[0] != ls[0]) | (ls[1] != ls[1]) | (ls[2] != ls[2]) | (ls[3] != ls[3]);
+    // (while every LSE so far is -inf, mn = m = -inf and every weight below
+    // is zero: no skip, whose branch would hold the loads above behind the
+    // LSE loads)
     const float mn = fmaxf(m, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
-    if (mn == -INFINITY) continue;
     if (mn != m) {
       const float sc = (m == -INFINITY) ? 0.f : expf(m - mn);
       tot *= sc;
