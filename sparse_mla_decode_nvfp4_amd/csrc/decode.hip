@@ -502,14 +502,23 @@ decode_tile16_kernel(DecodeArgs a) {
   }
   if (tile < tile1) step(cur, other, tile);
 
-  // ---- epilogue: denominators over lanes and waves, normalise, write
+  // ---- epilogue: denominators over lanes and waves, normalise, write.
+  // The sink logits of this lane's four O rows are requested first, all
+  // four together (loads under the per-row condition below would go out
+  // one round trip after another), and the barriers order LDS only (the
+  // last tile's unused prefetch need not land first).
+  float skv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.splits == 1 && a.sink != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) skv[r] = a.sink[h0 + 4 * g + r];
+  }
   float lt = l_part;
   lt += shfl_xor(lt, 16);
   lt += shfl_xor(lt, 32);
-  __syncthreads();
+  lds_barrier();                                  // every wave is done with the tiles
   if (g == 0) lsum[wave][n] = lt;
   if (wave == 0 && g == 0) tmax[0][n] = m_n;      // the agreed running max of head n
-  __syncthreads();
+  lds_barrier();
   const size_t orow = (size_t)row * a.h_q + h0;
   const size_t prow = ((size_t)split * a.rows + row) * a.h_q + h0;
   float inv[4];
@@ -519,7 +528,7 @@ decode_tile16_kernel(DecodeArgs a) {
     const float l = lsum[0][h] + lsum[1][h] + lsum[2][h] + lsum[3][h];
     float denom = l;
     if (a.splits == 1 && a.sink != nullptr && l > 0.f)
-      denom += exp2f(a.sink[h0 + h] * kLog2e - tmax[0][h]);
+      denom += exp2f(skv[r] * kLog2e - tmax[0][h]);
     inv[r] = l > 0.f ? 1.0f / denom : 0.f;
   }
   // Stage this wave's normalised block [16 heads][128 dv] in fp32 (rows
