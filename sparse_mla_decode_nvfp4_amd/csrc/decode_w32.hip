@@ -22,9 +22,9 @@
 //     16-head blocks sharing each K operand) goes through LDS to the other
 //     half of the pair; both halves add the two partials (bit-identical sums)
 //     and run the same online softmax; P moves to the 32x32 operand layout
-//     with one lane-row swap, and O += P V runs as 32x32x16 MFMAs on the
-//     wave's own V half, read transposed from a wave-private XOR-swizzled
-//     LDS tile;
+//     with one lane-row swap, and O^T += V^T P^T runs as 32x32x16 MFMAs on
+//     the wave's own V half, read transposed from a wave-private XOR-swizzled
+//     LDS tile (each lane accumulates one head's output dims);
 //   * Q is converted to fp16 once per workgroup with a per-head power-of-two
 //     scale folded into the softmax scale (exact for every bf16 element
 //     within 2^31 of its head's largest) and read from LDS as MFMA operands;
@@ -88,11 +88,8 @@ struct LdsW32 {
   // the sink logits of the group's 32 heads
   static constexpr int kOffSink = kOffFail + 16;
   static constexpr int kBytes = kOffSink + 32 * 4;
-  // merge: 4 slots of 4 KB per wave in round one, then an 8 KB output
-  // stage per wave (past the round-two slots for four pairs, from 0 for two)
-  static constexpr int kOffStage = kPairs == 4 ? 16 * 4096 : 0;
+  // merge: 4 slots of 4 KB per wave in round one
   static_assert(4 * kWaves * 4096 <= kOffStat, "merge slots overlap the statistics");
-  static_assert(kOffStage + kWaves * 8192 <= kOffStat, "output stage overlaps the statistics");
 };
 static_assert(LdsW32<2>::kBytes <= 80 * 1024, "two workgroups of two pairs must fit in a CU");
 
@@ -155,9 +152,6 @@ __device__ __forceinline__ uint32_t pack_f16p(float lo, float hi) {
 // V tile swizzle: 16-byte chunk j of row t lives at chunk j ^ vswz_p(t).
 __device__ __forceinline__ int vswz_p(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 
-// Row (head) of element r of a 32x32 accumulator in lane half kg.
-__device__ __forceinline__ int acc_row(int r, int kg) { return 8 * (r >> 2) + 4 * kg + (r & 3); }
-
 // Lane-row swaps (VALU): permlane16_swap(a, b) exchanges the odd 16-lane
 // rows of a with the even rows of b; permlane32_swap(a, b) exchanges the
 // upper 32 lanes of a with the lower 32 of b.
@@ -208,8 +202,9 @@ struct IntC {
 //     j = 8: RoPE dims 32hf + 8g..+7;
 //   A = K[token n][those dims], B = Q^T[same dims][head 16b+n],
 //   C = S^T[token 4g+r][head 16b+n] for head blocks b = 0, 1.
-//   PV (32x32x16): A = P[head tl][token 8kg+i], B = V[token 8kg+i][dv 32nb +
-//   tl], C = O[head acc_row(r, kg)][dv 256hf + 32nb + tl].
+//   PV (32x32x16), computed as O^T = V^T P^T: A = V^T[dv 32nb + tl][token
+//   8kg+i], B = P^T[token 8kg+i][head tl], C = O^T[dv 256hf + 32nb + 8(r>>2) +
+//   4kg + (r&3)][head tl]: a lane's 128 accumulators all belong to head tl.
 template <bool kDual, class F, int kPairs>
 __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_kernel(DecodeArgs a) {
   using L = LdsW32<kPairs>;
@@ -576,16 +571,13 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
         l_part[b] *= alpha[b];
         m_use[b] = m_new;
       }
-      float ar[16];
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int hr = acc_row(r, kg);
-        ar[r] = __shfl(hr < 16 ? alpha[0] : alpha[1], hr & 15);
-      }
+      // a lane's rows of O are all its head's (tl: head n for tl < 16,
+      // 16 + n otherwise)
+      const float al = tl < 16 ? alpha[0] : alpha[1];
 #pragma unroll
       for (int nb = 0; nb < 8; nb++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc_o[nb][r] *= ar[r];
+        for (int r = 0; r < 16; r++) acc_o[nb][r] *= al;
     }
     // P as fp16 hi + lo parts (the lo part holds P - hi exactly to fp16's
     // precision), so PV carries P to about 2^-22 instead of 2^-11
@@ -634,10 +626,10 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
       }
 #pragma unroll
       for (int u = 0; u < 2; u++)
-        acc_o[nb + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pL, bv[u], acc_o[nb + u], 0, 0, 0);
+        acc_o[nb + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[u], pL, acc_o[nb + u], 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < 2; u++)
-        acc_o[nb + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pA, bv[u], acc_o[nb + u], 0, 0, 0);
+        acc_o[nb + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[u], pA, acc_o[nb + u], 0, 0, 0);
     }
   };
 
@@ -707,10 +699,8 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     const float mown = mp[pr];
     fown = (mown == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mown - M);
   }
-  // this pair's weight on each accumulator row
-  float fr[16];
-#pragma unroll
-  for (int r = 0; r < 16; r++) fr[r] = __shfl(fown, acc_row(r, kg));
+  // this pair's weight: a lane's accumulators are all head hh's
+  const float fr = fown;
   // Two rounds of pairwise sums through LDS (slots of 16 floats x 64 lanes,
   // lane-contiguous, over the first 128 KB): round 1 pairs p and p^1 (even p
   // keeps blocks 0..3, odd p 4..7), round 2 pairs p and p^2 (each keeps two
@@ -724,8 +714,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     lds_f32x4* d = reinterpret_cast<lds_f32x4*>(lds + slot * 4096) + lane;
 #pragma unroll
     for (int rq = 0; rq < 4; rq++)
-      d[rq * 64] = f32x4{o[4 * rq] * fr[4 * rq], o[4 * rq + 1] * fr[4 * rq + 1], o[4 * rq + 2] * fr[4 * rq + 2],
-                         o[4 * rq + 3] * fr[4 * rq + 3]};
+      d[rq * 64] = f32x4{o[4 * rq] * fr, o[4 * rq + 1] * fr, o[4 * rq + 2] * fr, o[4 * rq + 3] * fr};
   };
   auto fma_add = [&](int slot, f32x16& o) {
     const lds_f32x4* d = reinterpret_cast<const lds_f32x4*>(lds + slot * 4096) + lane;
@@ -733,7 +722,7 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     for (int rq = 0; rq < 4; rq++) {
       const f32x4 t = d[rq * 64];
 #pragma unroll
-      for (int e = 0; e < 4; e++) o[4 * rq + e] = __builtin_fmaf(o[4 * rq + e], fr[4 * rq + e], t[e]);
+      for (int e = 0; e < 4; e++) o[4 * rq + e] = __builtin_fmaf(o[4 * rq + e], fr, t[e]);
     }
   };
   auto add = [&](int slot, f32x16& o) {
@@ -784,80 +773,63 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     }
   }
 
-  // ---- normalise and write this wave's two output blocks
-  float inv[16];
+  // ---- normalise and write this wave's output blocks.  Lane l holds head
+  // tl's values at dv 256hf + 32nb + 8q + 4kg + 0..3 (q = 0..3) of each
+  // block nb.  Packed to 16 bits and swapped between lane halves (the upper
+  // 32 lanes' q = 2p values with the lower 32's q = 2p+1 ones), a lane holds 8
+  // consecutive dv, 8q' + 0..7 with q' = 2p + kg, and stores them as 16 bytes.
+  float inv;
   {
     float denom = Lh;
     if (single && a.sink != nullptr && Lh > 0.f) denom += __builtin_amdgcn_exp2f(sinkl[hh] * kLog2eP - Mh);
-    float invh = Lh > 0.f ? 1.0f / denom : 0.f;
-    if (wg_failed) invh = __builtin_nanf("");
-#pragma unroll
-    for (int r = 0; r < 16; r++) inv[r] = __shfl(invh, acc_row(r, kg));
+    inv = Lh > 0.f ? 1.0f / denom : 0.f;
+    if (wg_failed) inv = __builtin_nanf("");
   }
   const size_t orow = (size_t)row * a.h_q + h0;
   const size_t prow = ((size_t)split * a.rows + row) * a.h_q + h0;
-  // Stage two of this wave's blocks at a time as [32 heads][64 dv] fp32
-  // (wave-private space past the merge slots still in use), then store rows
-  // of 8 dv per lane.  Column c of head row h sits at c ^ 32((h>>2)&1) ^
-  // 4(h&1): the two lane halves of a write (heads 4 apart) and neighbouring
-  // heads of a read use disjoint banks.
-  lds_f32* const stg = (lds_f32*)(lds + L::kOffStage + wave * 8192);
-  auto stage_blocks = [&](auto base_c) {
-    constexpr int kB = decltype(base_c)::value;
+  auto store_block = [&](auto nb_c) {
+    constexpr int kB = decltype(nb_c)::value;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    // two 16-bit values of run q, elements e, e+1
+    auto pack = [&](int q, int e) -> uint32_t {
+      const f32x2 v = {acc_o[kB][4 * q + e] * inv, acc_o[kB][4 * q + e + 1] * inv};
+      return single ? __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2))
+                    : __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    };
 #pragma unroll
-    for (int u = 0; u < 2; u++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int hr = acc_row(r, kg);
-        stg[hr * 64 + ((((u ^ kg) << 5) | tl) ^ ((r & 1) << 2))] = acc_o[kB + u][r] * inv[r];
-      }
-  };
-  auto store_blocks = [&](int kb) {
-    const int ch = lane & 7;                  // 8-dv chunk of the 64 staged dv
-    const int dv0 = 256 * hf + 32 * kb + 8 * ch;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int h = (lane >> 3) + 8 * i;
-      const int x = (((h >> 2) & 1) << 5) ^ ((h & 1) << 2);
-      const f32x4 lo = *reinterpret_cast<const lds_f32x4*>(stg + h * 64 + ((8 * ch) ^ x));
-      const f32x4 hi = *reinterpret_cast<const lds_f32x4*>(stg + h * 64 + ((8 * ch + 4) ^ x));
-      if (single) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const u32x4 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo.x, lo.y}, bf16x2)),
-                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo.z, lo.w}, bf16x2)),
-                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.x, hi.y}, bf16x2)),
-                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.z, hi.w}, bf16x2))};
-        *reinterpret_cast<u32x4*>(a.out + (orow + h) * kVDim + dv0) = v;
-      } else {
+    for (int p2 = 0; p2 < 2; p2++) {
+      // x: run 2p2 (lanes of kg 0: dv +0..3, kg 1: +4..7), y: run 2p2 + 1
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pack(2 * p2, 0), pack(2 * p2 + 1, 0), false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pack(2 * p2, 2), pack(2 * p2 + 1, 2), false, false);
+      // lanes of kg 0 now hold run 2p2's dv +0..7, lanes of kg 1 run 2p2+1's
+      const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+      const int dv = 256 * hf + 32 * kB + 8 * (2 * p2 + kg);
+      if (single)
+        *reinterpret_cast<u32x4*>(a.out + (orow + tl) * kVDim + dv) = v;
+      else
         // split partial in fp16: normalised within the split, so a convex
         // combination of V rows (|value| <= 6 * 448), rounded to nearest
-        const u32x4 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo.x, lo.y}, f16x2)),
-                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo.z, lo.w}, f16x2)),
-                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.x, hi.y}, f16x2)),
-                         __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{hi.z, hi.w}, f16x2))};
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o_part) + (prow + h) * kVDim + dv0) = v;
-      }
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o_part) + (prow + tl) * kVDim + dv) = v;
     }
   };
+  auto store_pair = [&](auto nb_c) {
+    constexpr int kB = decltype(nb_c)::value;
+    store_block(IntC<kB>{});
+    store_block(IntC<kB + 1>{});
+  };
   if constexpr (kPairs == 4) {
-    int kb;
     switch (pr) {
-      case 0: stage_blocks(IntC<0>{}); kb = 0; break;
-      case 1: stage_blocks(IntC<4>{}); kb = 4; break;
-      case 2: stage_blocks(IntC<2>{}); kb = 2; break;
-      default: stage_blocks(IntC<6>{}); kb = 6; break;
+      case 0: store_pair(IntC<0>{}); break;
+      case 1: store_pair(IntC<4>{}); break;
+      case 2: store_pair(IntC<2>{}); break;
+      default: store_pair(IntC<6>{}); break;
     }
-    store_blocks(kb);
   } else if (pr == 0) {
-    stage_blocks(IntC<0>{});
-    store_blocks(0);
-    stage_blocks(IntC<2>{});
-    store_blocks(2);
+    store_pair(IntC<0>{});
+    store_pair(IntC<2>{});
   } else {
-    stage_blocks(IntC<4>{});
-    store_blocks(4);
-    stage_blocks(IntC<6>{});
-    store_blocks(6);
+    store_pair(IntC<4>{});
+    store_pair(IntC<6>{});
   }
   if (wave == 0 && lane < 32) {
     float lse = Lh > 0.f ? (Mh + __log2f(Lh)) * kLn2P : -INFINITY;
