@@ -269,19 +269,19 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
   const int span = max(c_end - c_begin, 0);
   const RowSource<kDual> src(a, row);
 
-  // Chunks are numbered within the split and dealt in blocks of 18: pairs 0
-  // and 1 take 5 of each block (offsets p, p+4, p+8, p+12, 16+p), pairs 2 and
-  // 3 take 4 (p, p+4, p+8, p+12).  Pairs 0 and 1 are the first waves of their
-  // SIMDs, which issue first and run about 1.25 times as fast, so the pairs
-  // finish together; the fixed deal keeps the summation order, and so the
-  // result, the same on every run.  With two pairs (both the first, or both
-  // the second, waves of their SIMDs) the chunks alternate.  cid0..cid2 are
-  // this pair's chunks pos, pos+1 and pos+2.
-  const int kp = pr < 2 ? 5 : 4;
+  // Chunks are numbered within the split and dealt in blocks of 14: pairs 0
+  // and 1 take 4 of each block (offsets p, p+4, p+8, 12+p), pairs 2 and 3
+  // take 3 (p, p+4, p+8).  Pairs 0 and 1 are the first waves of their SIMDs,
+  // which issue first and run about 1.35 times as fast, so the pairs finish
+  // together; the fixed deal keeps the summation order, and so the result,
+  // the same on every run.  With two pairs (both the first, or both the
+  // second, waves of their SIMDs) the chunks alternate.  cid0..cid2 are this
+  // pair's chunks pos, pos+1 and pos+2.
+  const int kp = pr < 2 ? 4 : 3;
   auto cid_of = [&](int i) {
     if constexpr (kPairs == 2) return pr + 2 * i;
     const int blk = i / kp, j = i - blk * kp;
-    return 18 * blk + (j < 4 ? pr + 4 * j : 16 + pr);
+    return 14 * blk + (j < 3 ? pr + 4 * j : 12 + pr);
   };
   int cid0 = cid_of(0), cid1 = cid_of(1), cid2 = cid_of(2);
   // joined-list position of token n of chunk c
