@@ -28,8 +28,8 @@
 //     LDS so every wave applies the same running max; P goes to two shared
 //     tiles as fp16 hi + lo parts (PV runs on both, P carried to ~2^-22);
 //   * wave w accumulates O[16 heads, dv 128w .. 128w+127] over all 64 tokens
-//     of the tile (V read back with ds_read_b64_tr_b16), so the O accumulator
-//     is 32 registers per lane and two workgroups fit per CU;
+//     of the tile (V read back with ds_read_b64_tr_b16), as O^T so that a
+//     lane's 32 accumulators are one head's, and two workgroups fit per CU;
 //   * indices are prefetched two tiles ahead and token bytes one tile ahead;
 //   * the running max is only raised (and O rescaled) when a tile exceeds it
 //     by more than 2^8, so rescales are rare.
@@ -196,8 +196,9 @@ __device__ __forceinline__ h16x8 rope8_f16(uint32_t x, uint32_t y) {
 //   16*(4c+g) + 8*(ks&1) + [0,8) with c = ks/2 for lane group g (so a lane's
 //   blocks are {4c+g}, whose scales are the contiguous bytes 8g..8g+7);
 //   ks 16, 17 cover RoPE dims 16g + 8*(ks-16) + [0,8).  Q is laid out to match.
-//   PV (16x16x32): A = P[head n][token 32ks+8g+i], B = V[token 32ks+8g+i][dv],
-//   C = O[head 4g+r][dv 128w + 16nb + n].
+//   PV (16x16x32), computed as O^T = V^T P^T: A = V^T[dv 128w + 16nb + n][token
+//   32ks+8g+i], B = P^T[token 32ks+8g+i][head n], C = O^T[dv 128w + 16nb + 4g +
+//   r][head n]: a lane's 32 accumulators all belong to head n.
 template <bool kDual, class F>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 decode_tile16_kernel(DecodeArgs a) {
@@ -442,13 +443,11 @@ decode_tile16_kernel(DecodeArgs a) {
       m_n = tm_n;
     }
     if (__any(raise)) {
-      float alpha[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) alpha[r] = __shfl(alpha_n, 4 * g + r);
+      // every accumulator of a lane is head n's
 #pragma unroll
       for (int nb = 0; nb < 8; nb++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) acc_o[nb][r] *= alpha[r];
+        for (int r = 0; r < 4; r++) acc_o[nb][r] *= alpha_n;
     }
 
     // ---- P for this wave's tokens -> P tile (fp16)
@@ -485,10 +484,10 @@ decode_tile16_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < 2; u++)
-          acc_o[nb + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv[u], acc_o[nb + u], 0, 0, 0);
+          acc_o[nb + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[u], pl, acc_o[nb + u], 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 2; u++)
-          acc_o[nb + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[u], acc_o[nb + u], 0, 0, 0);
+          acc_o[nb + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[u], pa, acc_o[nb + u], 0, 0, 0);
       }
     }
     ok_cur = rn.ok;
@@ -503,64 +502,53 @@ decode_tile16_kernel(DecodeArgs a) {
   if (tile < tile1) step(cur, other, tile);
 
   // ---- epilogue: denominators over lanes and waves, normalise, write.
-  // The sink logits of this lane's four O rows are requested first, all
-  // four together (loads under the per-row condition below would go out
-  // one round trip after another), and the barriers order LDS only (the
-  // last tile's unused prefetch need not land first).
-  float skv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (a.splits == 1 && a.sink != nullptr) {
-#pragma unroll
-    for (int r = 0; r < 4; r++) skv[r] = a.sink[h0 + 4 * g + r];
-  }
+  // The sink logit of this lane's head is requested first, and the barriers
+  // order LDS only (the last tile's unused prefetch need not land first).
+  const float skv = (a.splits == 1 && a.sink != nullptr) ? a.sink[h0 + n] : 0.f;
   float lt = l_part;
   lt += shfl_xor(lt, 16);
   lt += shfl_xor(lt, 32);
   lds_barrier();                                  // every wave is done with the tiles
   if (g == 0) lsum[wave][n] = lt;
-  if (wave == 0 && g == 0) tmax[0][n] = m_n;      // the agreed running max of head n
   lds_barrier();
   const size_t orow = (size_t)row * a.h_q + h0;
   const size_t prow = ((size_t)split * a.rows + row) * a.h_q + h0;
-  float inv[4];
-#pragma unroll
-  for (int r = 0; r < 4; r++) {
-    const int h = 4 * g + r;
-    const float l = lsum[0][h] + lsum[1][h] + lsum[2][h] + lsum[3][h];
-    float denom = l;
-    if (a.splits == 1 && a.sink != nullptr && l > 0.f)
-      denom += exp2f(skv[r] * kLog2e - tmax[0][h]);
-    inv[r] = l > 0.f ? 1.0f / denom : 0.f;
+  const float lh = lsum[0][n] + lsum[1][n] + lsum[2][n] + lsum[3][n];
+  float inv;
+  {
+    float denom = lh;
+    if (a.splits == 1 && a.sink != nullptr && lh > 0.f) denom += exp2f(skv * kLog2e - m_n);
+    inv = lh > 0.f ? 1.0f / denom : 0.f;
   }
-  // Stage this wave's normalised block [16 heads][128 dv] in fp32 (rows
-  // padded to kStgRow floats: the 64 lanes of a column write hit 64 distinct
-  // banks) in the V tile, free since the first barrier above; it is
-  // wave-private, and a wave's LDS accesses complete in order.  Then each
-  // half-wave stores one head row of 128 dv: 4 values per lane.
-  constexpr int kStgRow = 132;
-  __attribute__((address_space(3))) float* const stg =
-      (__attribute__((address_space(3))) float*)(vtile + wave * (16 * kStgRow * 4));
+  // Lane (n, g) holds head n's values at dv 128w + 16nb + 4g + 0..3 of each
+  // block nb.  As fp32 partials they are stored as 16 bytes per block; as
+  // bf16, blocks nb and nb+1 are packed and swapped between neighbouring
+  // lane groups (odd groups' block nb with even groups' block nb+1), so that
+  // a lane holds 8 consecutive dv, 16 bytes: block nb + (g & 1), dv
+  // 16nb' + 8(g >> 1) + 0..7.
+  if (a.splits == 1) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    auto pack = [&](int nb, int e) -> uint32_t {
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(
+          f32x2{acc_o[nb][e] * inv, acc_o[nb][e + 1] * inv}, bf16x2));
+    };
 #pragma unroll
-  for (int nb = 0; nb < 8; nb++)
+    for (int nb = 0; nb < 8; nb += 2) {
+      const auto s0 = __builtin_amdgcn_permlane16_swap(pack(nb, 0), pack(nb + 1, 0), false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(pack(nb, 2), pack(nb + 1, 2), false, false);
+      const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+      const int dv = 128 * wave + 16 * (nb + (g & 1)) + 8 * (g >> 1);
+      *reinterpret_cast<u32x4*>(a.out + (orow + n) * kVDim + dv) = v;
+    }
+  } else {
 #pragma unroll
-    for (int r = 0; r < 4; r++) stg[(4 * g + r) * kStgRow + 16 * nb + n] = acc_o[nb][r] * inv[r];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int h = 2 * i + (lane >> 5);
-    const int c = lane & 31;                     // dv 4c .. 4c+3 of this wave's 128
-    const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(stg + h * kStgRow + 4 * c);
-    const int dv = 128 * wave + 4 * c;
-    if (a.splits == 1) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const u32x2 b = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v.x, v.y}, bf16x2)),
-                       __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v.z, v.w}, bf16x2))};
-      *reinterpret_cast<u32x2*>(a.out + (orow + h) * kVDim + dv) = b;
-    } else {
-      *reinterpret_cast<f32x4*>(a.o_part + (prow + h) * kVDim + dv) = v;
+    for (int nb = 0; nb < 8; nb++) {
+      const f32x4 v = {acc_o[nb][0] * inv, acc_o[nb][1] * inv, acc_o[nb][2] * inv, acc_o[nb][3] * inv};
+      *reinterpret_cast<f32x4*>(a.o_part + (prow + n) * kVDim + 128 * wave + 16 * nb + 4 * g) = v;
     }
   }
   if (wave == 0 && g == 0) {
-    const float l = lsum[0][n] + lsum[1][n] + lsum[2][n] + lsum[3][n];
-    const float lse = l > 0.f ? (m_n + log2f(l)) * kLn2 : -INFINITY;
+    const float lse = lh > 0.f ? (m_n + log2f(lh)) * kLn2 : -INFINITY;
     if (a.splits == 1) a.lse[orow + n] = lse;
     else a.lse_part[prow + n] = lse;
   }
