@@ -54,7 +54,12 @@ __device__ __forceinline__ RecRef resolve_rec(const DecodeArgs& a, int32_t v, bo
     return {a.cache + (ok ? a.pa.offset((uint32_t)v) : 0), ok};
   } else {
     const bool extra = p >= topk0;
-    const bool ok = in_list && v >= 0 && (int64_t)v < (extra ? a.num_slots1 : a.num_slots);
+    // both bounds compared, then the results selected: a per-lane select of
+    // the two bounds lets the compiler turn them into a per-lane vector load
+    // of the kernel argument, and that load waits for every gather in flight
+    const bool below0 = (int64_t)v < a.num_slots;
+    const bool below1 = (int64_t)v < a.num_slots1;
+    const bool ok = in_list && v >= 0 && (extra ? below1 : below0);
     const uint32_t slot = ok ? (uint32_t)v : 0u;
     const uint8_t* r0 = a.cache + a.pa.offset(slot);
     const uint8_t* r1 = a.cache1 + a.pa1.offset(slot);
