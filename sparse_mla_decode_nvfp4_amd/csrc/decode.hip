@@ -427,44 +427,52 @@ decode_tile16_kernel(DecodeArgs a) {
     bm = fmaxf(bm, shfl_xor(bm, 16));
     bm = fmaxf(bm, shfl_xor(bm, 32));
     if (g == 0) tmax[wave][n] = bm;
-    lds_barrier();                        // every wave's maxima posted
 
-    // ---- running max update (same rule in every wave), lazy O rescale.
-    // The O rows' factors come from the lanes of their heads, only when some
-    // head's max was raised.
+    // ---- P for this wave's tokens -> P tiles (fp16 hi + lo parts, so PV
+    // carries P to about 2^-22), computed with the running max as it stands.
+    // It stays valid unless the tile raises the max; the barrier below posts
+    // every wave's tile maxima with the P and V tiles, and only a raise (the
+    // same decision in every wave, a rare event after the first tile) pays
+    // for recomputing P and a second barrier.
+    float p[4];
+    auto write_p = [&]() {
+      const float m_safe = (m_n == -INFINITY) ? 0.f : m_n;   // s = -inf -> p = 0
+#pragma unroll
+      for (int r = 0; r < 4; r++) p[r] = fast_exp2(s[r] - m_safe);
+      const h16x2 h01 = __builtin_convertvector(f32x2{p[0], p[1]}, h16x2);
+      const h16x2 h23 = __builtin_convertvector(f32x2{p[2], p[3]}, h16x2);
+      const f32x2 f01 = __builtin_convertvector(h01, f32x2), f23 = __builtin_convertvector(h23, f32x2);
+      *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) =
+          u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      *reinterpret_cast<u32x2*>(&ptile_lo[n][16 * wave + 4 * g]) =
+          u32x2{pack_h16x2(p[0] - f01.x, p[1] - f01.y), pack_h16x2(p[2] - f23.x, p[3] - f23.y)};
+    };
+    write_p();
+    lds_barrier();                        // maxima, P and V tiles complete
+
+    // ---- running max update (same rule in every wave), lazy O rescale:
+    // every accumulator of a lane is head n's
     float tm_n = tmax[0][n];
 #pragma unroll
     for (int w = 1; w < kWaves; w++) tm_n = fmaxf(tm_n, tmax[w][n]);
     const bool raise = tm_n > m_n + kLazyThreshold;
-    float alpha_n = 1.0f;
-    if (raise) {
-      alpha_n = fast_exp2(m_n - tm_n);    // m_n = -inf gives 0 (l_part and O are 0 then)
-      l_part *= alpha_n;
-      m_n = tm_n;
-    }
     if (__any(raise)) {
-      // every accumulator of a lane is head n's
+      // every wave holds the same m_n and reads the same maxima, so every
+      // wave takes this branch or none does
+      float alpha_n = 1.0f;
+      if (raise) {
+        alpha_n = fast_exp2(m_n - tm_n);  // m_n = -inf gives 0 (l_part and O are 0 then)
+        l_part *= alpha_n;
+        m_n = tm_n;
+      }
 #pragma unroll
       for (int nb = 0; nb < 8; nb++)
 #pragma unroll
         for (int r = 0; r < 4; r++) acc_o[nb][r] *= alpha_n;
+      write_p();
+      lds_barrier();                      // P tiles rewritten
     }
-
-    // ---- P for this wave's tokens -> P tile (fp16)
-    const float m_safe = (m_n == -INFINITY) ? 0.f : m_n;   // s = -inf -> p = 0
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) p[r] = fast_exp2(s[r] - m_safe);
     l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    // P as fp16 hi + lo parts, so PV carries P to about 2^-22
-    const h16x2 h01 = __builtin_convertvector(f32x2{p[0], p[1]}, h16x2);
-    const h16x2 h23 = __builtin_convertvector(f32x2{p[2], p[3]}, h16x2);
-    const f32x2 f01 = __builtin_convertvector(h01, f32x2), f23 = __builtin_convertvector(h23, f32x2);
-    *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) =
-        u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-    *reinterpret_cast<u32x2*>(&ptile_lo[n][16 * wave + 4 * g]) =
-        u32x2{pack_h16x2(p[0] - f01.x, p[1] - f01.y), pack_h16x2(p[2] - f23.x, p[3] - f23.y)};
-    lds_barrier();                        // P and V tiles complete
 
     // ---- O[:, 128w .. 128w+127] += P V over the tile's 64 tokens
 #pragma unroll
