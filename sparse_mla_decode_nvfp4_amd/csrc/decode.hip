@@ -500,6 +500,9 @@ decode_tile16_kernel(DecodeArgs a) {
     }
     ok_cur = rn.ok;
     idx_nxt = idx_nn;
+    // keep the next step's index checks out of this step's PV: there they
+    // wait for the index load issued at the top of this step
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   RawTok<F> other;

@@ -433,8 +433,9 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
     const RecRef rn = resolve_rec<kDual>(a, nxt_raw, chunk_ok(cid1), tok_pos(cid1), src.topk0);
     const uint8_t* const rec_next = rn.ptr;
     // block scales of this lane; zero for an invalid token, so its V row is
-    // zero
-    const uint32_t sw = v ? cur.scales(ssel) : 0u;
+    // zero (a mask, not a select: the compiler turns the select into a branch
+    // around the byte permutes, whose join waits for more of the gathers)
+    const uint32_t sw = cur.scales(ssel) & (0u - (uint32_t)v);
     // the four block scales as fp16 (exact), two per convert
     const f16x2 sp[2] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false),
                          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)};

@@ -104,6 +104,24 @@ def test_large_scores_raise_the_running_max(lib, h, splits):
     assert_decode_close(o, lse, o_ref, l_ref, f"large scores h{h}")
 
 
+@pytest.mark.parametrize("h,splits", [(16, 1), (48, 1), (32, 1), (64, 2)])
+def test_scores_rising_along_the_list_raise_the_max_in_every_tile(lib, h, splits):
+    # the index list ordered by head 0's score, lowest first, with scores
+    # spread over hundreds of log2 units: head 0's running max is raised in
+    # nearly every tile (16-head kernel) or chunk (32-head kernel), so the
+    # raise path (rescale and, in the 16-head kernel, P redone behind a
+    # second barrier) runs all along the list
+    note(f"rising scores h={h} splits={splits}")
+    recs, q, idx, sink, nb, bs = small_case(47, 1, 2, h, 700, p_inval=0.0)
+    q = (q.float() * 24.0).to(torch.bfloat16)
+    k = OC.dequantize_records(recs)                       # [slots, 576] fp64
+    for r in range(idx.shape[1]):
+        s0 = k[idx[0, r]] @ f64(q)[0, r, 0]
+        idx[0, r] = idx[0, r][np.argsort(s0, kind="stable")]
+    o, lse, o_ref, l_ref = run_small(lib, recs, q, idx, sink, nb, bs, splits)
+    assert_decode_close(o, lse, o_ref, l_ref, f"rising scores h{h}")
+
+
 def test_split_counts_agree(lib):
     recs, q, idx, sink, nb, bs = small_case(21, 1, 2, 64, 1024)
     outs = []
