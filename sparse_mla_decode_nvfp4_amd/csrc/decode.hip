@@ -14,7 +14,7 @@
 //     the top-k list, and walks it in 64-token tiles; wave w loads and
 //     dequantizes tokens [16w, 16w+16) of each tile;
 //   * a lane loads the bytes of one token it needs straight from HBM (64
-//     NoPE bytes, the scale area, 16 RoPE values) and dequantizes them to
+//     NoPE bytes, half the scale area, 16 RoPE values) and dequantizes them to
 //     fp16 QK operands: every E2M1 x E4M3 product has at most 6 significant
 //     bits and lies in [2^-10, 2688], so it is exact in fp16 (the codes
 //     convert exactly, the scales convert exactly to fp16, one packed
@@ -94,14 +94,16 @@ __device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
 // 432-byte record their scales are the eight bytes 256 + 8g .. (block
 // order).  In the 352-byte record block s's scale sits at 320 + 8(s&3) +
 // (s>>2), so the lane's scales are the 16-bit words at 320 + 8k + 2g (k =
-// 0..3): word k holds blocks 8g+k (low byte) and 8g+4+k (high byte); the lane
-// loads the whole 32-byte scale area and picks them out.
+// 0..3): word k holds blocks 8g+k (low byte) and 8g+4+k (high byte), in
+// scale dword 2k + (g>>1).  Lanes 0..31 (g = 0, 1) load scale dwords 0..3 and
+// lanes 32..63 dwords 4..7, one 16-byte gather each; a swap between the lane
+// halves then leaves every lane the four dwords of its parity.
 template <class F>
 struct RawTok;
 template <>
 struct RawTok<Fmt352> {
   u32x4 nope[4];         // NoPE bytes 64g + 16i .. +15
-  u32x4 sc[2];           // scale area, bytes 0 .. 31
+  u32x4 sc;              // scale area bytes 16(g>>1) .. +15
   u32x4 rope;            // RoPE elements 16g .. 16g+15 (E4M3)
 };
 template <>
@@ -117,12 +119,16 @@ __device__ __forceinline__ int blk(int g, int c) { return 8 * g + c; }
 // Scale bytes of blocks 8g .. 8g+3 (x) and 8g+4 .. 8g+7 (y), one byte each.
 __device__ __forceinline__ u32x2 block_scales(const RawTok<Fmt432>& t, int) { return t.scale; }
 __device__ __forceinline__ u32x2 block_scales(const RawTok<Fmt352>& t, int g) {
-  const bool second = (g >> 1) != 0;              // word in the second dword of its 8 bytes
+  // Lane halves swap dwords 1 and 3 of the lower half's load with dwords 0
+  // and 2 of the upper half's: afterwards scale dword 2k + (g>>1) is word k of
+  // every lane (the lower half keeps the even dwords, the upper the odd).
+  const auto s01 = __builtin_amdgcn_permlane32_swap(t.sc.x, t.sc.y, false, false);
+  const auto s23 = __builtin_amdgcn_permlane32_swap(t.sc.z, t.sc.w, false, false);
   const uint32_t sh = 16u * (uint32_t)(g & 1);
-  const uint32_t w0 = (second ? t.sc[0].y : t.sc[0].x) >> sh;
-  const uint32_t w1 = (second ? t.sc[0].w : t.sc[0].z) >> sh;
-  const uint32_t w2 = (second ? t.sc[1].y : t.sc[1].x) >> sh;
-  const uint32_t w3 = (second ? t.sc[1].w : t.sc[1].z) >> sh;
+  const uint32_t w0 = s01[0] >> sh;
+  const uint32_t w1 = s23[0] >> sh;
+  const uint32_t w2 = s01[1] >> sh;
+  const uint32_t w3 = s23[1] >> sh;
   // byte i of perm(a, b, sel) is byte sel_i of the 8-byte value {a : b}
   const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u) |
                       (__builtin_amdgcn_perm(w3, w2, 0x0c0c0400u) << 16);
@@ -154,8 +160,7 @@ __device__ __forceinline__ void load_tok_tail(RawTok<F>& t, const uint8_t* rec, 
     t.rope[0] = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 32 * g);
     t.rope[1] = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 32 * g + 16);
   } else {
-    t.sc[0] = *reinterpret_cast<const u32x4*>(rec + F::kScaleOff);
-    t.sc[1] = *reinterpret_cast<const u32x4*>(rec + F::kScaleOff + 16);
+    t.sc = *reinterpret_cast<const u32x4*>(rec + F::kScaleOff + 16 * (g >> 1));
     t.rope = *reinterpret_cast<const u32x4*>(rec + F::kRopeOff + 16 * g);
   }
 }
