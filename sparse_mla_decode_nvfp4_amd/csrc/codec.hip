@@ -27,6 +27,22 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_mag(float q) {
   return (b >> 20) - (120u << 3);            // rebias exponent 127 -> 7
 }
 
+// The block scale byte E4M3(amax / 6), rounded once from the exact quotient
+// (ties to even, saturating at 448) without a division:
+//   * q = amax * fl(1/6) is within 2^-23 of amax / 6, relative;
+//   * a midpoint m of the E4M3 grid has at most 5 significant bits, so amax /
+//     6 is a tie only when amax = 6 m exactly (6 m has at most 7 significant
+//     bits); every other bf16 or fp16 amax (at most 11 significant bits)
+//     differs from 6 m by at least 2^-11 relative;
+//   * so rounding q to 16 significant bits returns every tie exactly and
+//     leaves every other quotient on its side of every midpoint.
+// The minimum comes first, so a NaN (or infinite) amax saturates to 448.
+__device__ __forceinline__ uint32_t e4m3_scale_of_amax(float amax) {
+  float q = fminf(amax * (1.0f / 6.0f), 448.0f);
+  q = __uint_as_float((__float_as_uint(q) + 0x80u) & 0xFFFFFF00u);
+  return e4m3_rne_sat_mag(q);
+}
+
 // The E2M1 code of x / s, rounded to nearest with ties to the even code,
 // comes from the hardware fp32 -> E2M1 convert (round to nearest even,
 // saturating at 6, sign kept, including for zero) applied to a quotient that
@@ -128,7 +144,7 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
   static_assert(!(kF16 && F::kBf16Rope), "the 432-byte record holds bf16 RoPE");
   static_assert(!(kF16 && kFused), "the fused path takes bf16 inputs");
   __shared__ __attribute__((aligned(16))) uint8_t rec[4][F::kBytes];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: token math in scalar registers
   const int lane = threadIdx.x & 63;
   const int64_t tok0 = ((int64_t)blockIdx.x * 4 + wave) * kTokW;
   if (tok0 >= num_tokens) return;
@@ -179,7 +195,7 @@ quantize_append_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
 #pragma unroll
     for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1));
-    const uint32_t scode = e4m3_rne_sat_mag(__fdiv_rn(amax, 6.0f));
+    const uint32_t scode = e4m3_scale_of_amax(amax);
     const float sv = e4m3x2_to_f32<0>(scode).x;
     const float rs = sv == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sv);
     // codes 2i (low nibble) and 2i+1 of byte i
@@ -223,7 +239,7 @@ __global__ void __launch_bounds__(256)
 dequantize_gather_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, PageAddr pa,
                          const int32_t* __restrict__ slots, int64_t n,
                          uint16_t* __restrict__ out) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: token math in scalar registers
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= n) return;
@@ -304,7 +320,7 @@ __global__ void __launch_bounds__(256)
 norm_rope_f32_kernel(const uint16_t* __restrict__ latent, int64_t lstride,
                      const uint16_t* __restrict__ rope, int64_t rstride, NormRope nr,
                      int64_t num_tokens, float* __restrict__ out) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: token math in scalar registers
   const int lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
   if (tok >= num_tokens) return;
