@@ -84,10 +84,6 @@ __device__ __forceinline__ void lds_barrier() {
 // weights that may flush to zero).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, h16x2));
-}
-
 // The bytes one lane needs of one token record.  Lane group g takes NoPE
 // blocks 8g .. 8g+7: 64 contiguous bytes, four 16-byte loads (few, wide
 // gathers: the address unit, not HBM, limits this kernel's loads).  In the
@@ -170,7 +166,6 @@ __device__ __forceinline__ void load_tok(RawTok<F>& t, const uint8_t* rec, int g
   for (int i = 0; i < 4; i++) load_tok_nope(t, rec, g, i);
   load_tok_tail(t, rec, g);
 }
-
 
 // Eight E2M1 codes times a block scale -> eight fp16, exact: the codes
 // convert exactly, the scale is an E4M3 value held exactly in fp16, and their
@@ -444,13 +439,11 @@ decode_tile16_kernel(DecodeArgs a) {
       const float m_safe = (m_n == -INFINITY) ? 0.f : m_n;   // s = -inf -> p = 0
 #pragma unroll
       for (int r = 0; r < 4; r++) p[r] = fast_exp2(s[r] - m_safe);
-      const h16x2 h01 = __builtin_convertvector(f32x2{p[0], p[1]}, h16x2);
-      const h16x2 h23 = __builtin_convertvector(f32x2{p[2], p[3]}, h16x2);
-      const f32x2 f01 = __builtin_convertvector(h01, f32x2), f23 = __builtin_convertvector(h23, f32x2);
-      *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) =
-          u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-      *reinterpret_cast<u32x2*>(&ptile_lo[n][16 * wave + 4 * g]) =
-          u32x2{pack_h16x2(p[0] - f01.x, p[1] - f01.y), pack_h16x2(p[2] - f23.x, p[3] - f23.y)};
+      uint32_t hi[2], lo[2];
+      split_p(p[0], p[1], hi[0], lo[0]);
+      split_p(p[2], p[3], hi[1], lo[1]);
+      *reinterpret_cast<u32x2*>(&ptile[n][16 * wave + 4 * g]) = u32x2{hi[0], hi[1]};
+      *reinterpret_cast<u32x2*>(&ptile_lo[n][16 * wave + 4 * g]) = u32x2{lo[0], lo[1]};
     };
     write_p();
     lds_barrier();                        // maxima, P and V tiles complete

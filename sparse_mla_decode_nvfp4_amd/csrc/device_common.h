@@ -118,4 +118,19 @@ struct PageAddr {
   }
 };
 
+typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
+
+// P = hi + lo for a pair of fp32 values: hi = fp16(p) packed, lo = fp16(p -
+// hi) packed.  p - hi is exact in fp32 (hi is p rounded to 11 significant
+// bits), so each mixed-precision FMA (-1 * hi + p, hi read as fp16, rounded
+// once to fp16) gives the same bits as subtracting in fp32 and converting:
+// three instructions per pair instead of six.
+__device__ __forceinline__ void split_p(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, h16x2_t));
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi), "v"(p0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(hi), "v"(p1));
+  lo = r;
+}
+
 }  // namespace nvfp4
