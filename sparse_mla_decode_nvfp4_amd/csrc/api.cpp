@@ -111,6 +111,7 @@ nvfp4::PageAddr make_page_addr(int32_t block_size, int64_t block_stride_bytes,
   pa.block_stride = (uint64_t)block_stride_bytes;
   pa.block_size = (uint32_t)block_size;
   pa.pow2 = (block_size & (block_size - 1)) == 0;
+  pa.contig = (uint64_t)block_stride_bytes == (uint64_t)block_size * (uint64_t)record_bytes;
   pa.shift = 0;
   while ((1u << pa.shift) < (uint32_t)block_size) pa.shift++;
   // ceil(2^64 / d) for d >= 2 that is not a power of two

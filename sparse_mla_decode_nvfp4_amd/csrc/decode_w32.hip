@@ -387,6 +387,9 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
 
   f32x16 acc_o[8];
   float m_use[2] = {-INFINITY, -INFINITY};    // running max (log2 units) of heads n, 16+n
+  // the exponent offset of P: -m_use, or 0 while m_use is -inf (every
+  // score so far masked); changes only when the max is raised
+  float neg_m[2] = {0.f, 0.f};
   float l_part[2] = {0.f, 0.f};
 
   // V tile: k-step j of row n is 16-byte chunk 8g + j of the half-row
@@ -571,25 +574,29 @@ __global__ void __launch_bounds__(128 * kPairs, kPairs == 4 ? 1 : 2) decode_w32_
         alpha[b] = (m_new == m_use[b]) ? 1.0f : __builtin_amdgcn_exp2f(m_use[b] - m_new);
         l_part[b] *= alpha[b];
         m_use[b] = m_new;
+        neg_m[b] = (m_new == -INFINITY) ? 0.f : -m_new;
       }
       // a lane's rows of O are all its head's (tl: head n for tl < 16,
-      // 16 + n otherwise)
-      const float al = tl < 16 ? alpha[0] : alpha[1];
+      // 16 + n otherwise).  Before the pair's first PV, O is all +0 and
+      // stays so: the first chunk, which always raises the max, skips the
+      // multiplies
+      if (pos > 0) {
+        const float al = tl < 16 ? alpha[0] : alpha[1];
 #pragma unroll
-      for (int nb = 0; nb < 8; nb++)
+        for (int nb = 0; nb < 8; nb++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc_o[nb][r] *= al;
+          for (int r = 0; r < 16; r++) acc_o[nb][r] *= al;
+      }
     }
     // P as fp16 hi + lo parts (the lo part holds P - hi exactly to fp16's
     // precision), so PV carries P to about 2^-22 instead of 2^-11
     uint32_t pd[2][2], pl[2][2];
 #pragma unroll
     for (int b = 0; b < 2; b++) {
-      const float ms = (m_use[b] == -INFINITY) ? 0.f : m_use[b];
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], qscale[b], -ms));
+        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], qscale[b], neg_m[b]));
         l_part[b] += p[r];
       }
 #pragma unroll

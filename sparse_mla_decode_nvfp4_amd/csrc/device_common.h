@@ -92,9 +92,11 @@ __device__ __forceinline__ void dequant8(uint32_t nib, float scale, uint32_t out
 
 // Slot -> byte offset of its record in the paged cache.  Pages of
 // `block_size` records of `record_bytes` each start every `block_stride`
-// bytes.  Power-of-two page
-// sizes use shift/mask; others use a 64-bit reciprocal (exact for every
-// 32-bit slot: floor(n * ceil(2^64/d) / 2^64) == n / d).
+// bytes.  Unpadded pages (stride = block_size * record_bytes) make the
+// offset slot * record_bytes, one multiply; padded power-of-two page sizes
+// use shift/mask; others use a 64-bit reciprocal (exact for every 32-bit
+// slot: floor(n * ceil(2^64/d) / 2^64) == n / d).  The case flags are
+// kernel arguments, so the choice is one uniform branch.
 struct PageAddr {
   uint64_t block_stride;
   uint64_t recip;        // ceil(2^64 / block_size), unused for powers of two
@@ -102,7 +104,10 @@ struct PageAddr {
   uint32_t shift;        // log2(block_size) when pow2
   uint32_t pow2;
   uint32_t record_bytes; // 352 or 432
+  uint32_t contig;       // block_stride == block_size * record_bytes
+  uint32_t pad_;
   __device__ __forceinline__ uint64_t offset(uint32_t slot) const {
+    if (contig) return (uint64_t)slot * record_bytes;
     uint32_t page, off;
     if (pow2) {
       page = slot >> shift;
