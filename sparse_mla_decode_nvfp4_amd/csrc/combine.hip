@@ -41,8 +41,9 @@ constexpr int kWavesC = 4;
 //
 // Workgroups are dealt to the 8 XCDs round-robin by blockIdx.  The decode
 // kernels run every workgroup of row r on XCD r % 8 when the row count is a
-// multiple of 8, so with xcd_rows the blocks of row r go there too and read
-// the partials from that XCD's L2.
+// multiple of 8, and with xcd_rows the blocks of row r go there too.  The
+// partials are not found in that XCD's L2 after the launch boundary, though:
+// by rocprofv3 FETCH_SIZE the combine fetches all of them from beyond L2.
 template <typename T>
 __global__ void __launch_bounds__(64 * kWavesC)
 combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
